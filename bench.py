@@ -1,0 +1,195 @@
+"""Throughput of the Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m]
+
+A step is one whole Muon step (momentum, norm, five Newton-Schulz rounds, update) over
+every matrix of the workload, on inputs already resident in HBM (weights, fp32 momentum and
+two staged gradient batches used alternately). Prints one JSON line:
+
+  value      Muon steps/s over K timed steps (HIP events on the library's stream,
+             bracketed by device synchronisation)
+  roofline   the dominant kernel kind: algorithmic flops (or bytes) of its launches divided
+             by their summed duration, measured with the library's per-launch HIP events in
+             a second timed pass, against the MI355X peak
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def kind_work(wl, ns_steps=5):
+    """Algorithmic work per step of each kernel kind: flops for the products (nominal,
+    m <= n: gram 2 m^2 n, poly 2 m^3, apply 2 m^2 n per round), bytes for the elementwise
+    kernels (momentum: read G, read+write fp32 M; update: read+write W)."""
+    w = {"gram": 0.0, "poly": 0.0, "apply": 0.0, "momentum": 0.0, "update": 0.0, "norm": 0.0}
+    esz = 2 if wl.dtype == "bf16" else 4
+    for r, c in wl.shapes:
+        m, n = min(r, c), max(r, c)
+        w["gram"] += ns_steps * 2.0 * m * m * n
+        w["poly"] += ns_steps * 2.0 * m ** 3
+        w["apply"] += ns_steps * 2.0 * m * m * n
+        w["momentum"] += r * c * (esz + 8.0)
+        w["update"] += r * c * (2.0 * esz)
+    return w
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle, as it stands, on whole matrices of the workload (one step from zero
+    momentum each), in workload order until ``budget_s`` is spent; scaled to one full step
+    by nominal Newton-Schulz flops."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()
+                    if i.get("user_api") == "blas")
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    done_flops, used = 0.0, 0
+    for i, (r, c) in enumerate(wl.shapes):
+        W, G = si.weight(wl, i), si.grad(wl, i, 0)
+        t1 = time.perf_counter()
+        oracle.muon_step(W, np.zeros((r, c)), G)
+        m, n = min(r, c), max(r, c)
+        done_flops += 5 * (4.0 * m * m * n + 2.0 * m ** 3)
+        used = i + 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+        del t1
+    elapsed = time.perf_counter() - t0
+    frac = done_flops / wl.ns_flops_per_step()
+    sec_per_step = elapsed / frac
+    return {"value": 1.0 / sec_per_step, "unit": "Muon steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"float64 oracle, one step of matrices 0..{used - 1} of {wl.name} "
+                      f"({used}/{wl.n} matrices, {frac * 100:.1f}% of the step's nominal flops,"
+                      f" input generation included), scaled to the full step by flops; "
+                      f"{elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2_124m", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = si.WORKLOADS[args.workload]
+    n = wl.n
+    print(f"[bench] {wl.name}: {n} matrices, {wl.elements() / 1e6:.1f} M elements, "
+          f"generating inputs", file=sys.stderr, flush=True)
+    W = [si.weight(wl, i).to(dev) for i in range(n)]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in wl.shapes]
+    G = [[si.grad(wl, i, t).to(dev) for i in range(n)] for t in range(2)]
+    plan = MuonPlan(wl.shapes, [w.dtype for w in W], [w.dtype for w in W], args.precision, dev)
+    cfg = make_config()
+    stream = torch.cuda.current_stream()
+    print(f"[bench] workspace {plan.ws_bytes / 2**20:.1f} MiB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+
+    for t in range(args.warmup):
+        plan.step(W, G[t % 2], M, cfg)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for t in range(args.steps):
+        plan.step(W, G[t % 2], M, cfg)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = start.elapsed_time(stop) / args.steps
+    print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    work = kind_work(wl)
+    ns_flops = wl.ns_flops_per_step()
+    out = {
+        "metric": "Muon steps/s on GPT-2-124M matrix set; NS TFLOP/s as % bf16 MFMA peak",
+        "value": 1000.0 / ms, "unit": "Muon steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if args.precision == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1e-3) gradients, 2 staged batches)",
+        "config": {"workload": wl.name, "matrices": n,
+                   "shapes": sorted({f"{r}x{c}": 0 for r, c in wl.shapes}),
+                   "ns_steps": 5, "lr": 0.02, "beta": 0.95, "nesterov": True,
+                   "precision": args.precision},
+        "ns_tflops_whole_step": ns_flops / (ms * 1e-3) / 1e12,
+    }
+
+    if not args.no_profile:
+        plan.set_profiling(True)
+        for t in range(args.steps):
+            plan.step(W, G[t % 2], M, cfg)
+        torch.cuda.synchronize()
+        prof = plan.read_profile()
+        plan.set_profiling(False)
+        kernels = {}
+        for k, (kms, launches) in prof.items():
+            per_step = kms / args.steps
+            kernels[k] = {"ms_per_step": per_step, "launches_per_step": launches / args.steps,
+                          "avg_launch_us": 1e3 * kms / max(launches, 1)}
+        gemm_ms = sum(prof[k][0] for k in ("gram", "poly", "apply")) / args.steps
+        out["kernels"] = kernels
+        out["ns_tflops_kernels"] = ns_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+        peak_mm = PEAK_BF16_TFLOPS if args.precision == "bf16" else PEAK_F32_TFLOPS
+        out["ns_frac_of_peak"] = (out["ns_tflops_kernels"] or 0) / peak_mm
+        dom = max(prof, key=lambda k: prof[k][0])
+        dms, dl = prof[dom]
+        if dom in ("gram", "poly", "apply"):
+            ach = work[dom] * args.steps / (dms * 1e-3) / 1e12
+            out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak_mm,
+                               "unit": "TFLOP/s", "frac": ach / peak_mm, "traffic": None,
+                               "avg_launch_us": 1e3 * dms / max(dl, 1),
+                               "work_per_launch": work[dom] * args.steps / max(dl, 1)}
+        else:
+            ach = work.get(dom, 0.0) * args.steps / (dms * 1e-3) / 1e9
+            out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach,
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                               "traffic": None, "avg_launch_us": 1e3 * dms / max(dl, 1)}
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    out["host"] = {"cpu": platform.processor() or platform.machine(),
+                   "cpu_count": os.cpu_count(), "torch": torch.__version__,
+                   "hip": torch.version.hip,
+                   "gpu": torch.cuda.get_device_name(dev)}
+    plan.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

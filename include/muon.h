@@ -1,0 +1,159 @@
+/*
+ * muon.h - C ABI of an MI355X (gfx950) library that performs one Muon optimizer step over a
+ * list of 2-D weight matrices.
+ *
+ * The step, as the pages describe it:
+ *   - page "深入解析KellerJordan/modded-nanogpt中的训练架构与优化技术", section
+ *     "Muon优化器：动量正交化技术", subsection "核心算法": an optimizer with defaults
+ *     lr = 0.02, momentum = 0.95, nesterov = true, ns_steps = 5, whose step is (1) a
+ *     standard SGD momentum update, (2) Newton-Schulz orthogonalisation, (3) the parameter
+ *     update;
+ *   - same page, subsection "Newton-Schulz正交化": ns_steps rounds of A = X X^T,
+ *     B = b A + c A A, X = a X + B X with (a, b, c) = (3.4445, -4.7750, 2.0315), run in
+ *     bfloat16;
+ *   - page "Muon优化器与FP8混合精度：AI训练能效革命与绿色计算新范式", section
+ *     "Muon优化器的能效突破": Muon is momentum orthogonalised by Newton-Schulz.
+ *
+ * What one call computes for every matrix (W param, G grad, M momentum, all rows x cols):
+ *   M <- beta * M + G                                (fp32 buffer, fp32 arithmetic)
+ *   U  = G + beta * M  if nesterov, else U = M
+ *   X  = U / (||U||_F + eps)                         (Frobenius pre-normalisation; the
+ *        printed iteration omits it, and the record analysis at lqnn.cn, section 3.2,
+ *        names Frobenius normalisation in front of the quintic maps)
+ *   if rows > cols the iteration runs on X^T (wide form) and the result is transposed back
+ *   ns_steps rounds of the quintic iteration above
+ *   W <- W - lr * O                                  (O = the iteration's result)
+ *
+ * Conventions shared by every entry point:
+ *   - All buffers are device memory on the current HIP device, row-major, contiguous, with
+ *     16-byte aligned base addresses. The caller owns every buffer.
+ *   - Work is enqueued on `stream` and the call returns without synchronising. Buffers must
+ *     stay alive and untouched by other work until the stream has passed the call.
+ *   - Calls on one plan must be ordered (same stream, or synchronised between calls).
+ *   - Arguments are validated on the host before anything is enqueued: a call that returns
+ *     an error has enqueued nothing. muon_last_error() then describes the failure.
+ *   - NaN and Inf are propagated, not checked; they never leak from one matrix into another.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct muon_plan muon_plan; /* opaque; holds host metadata only */
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, overlap, mismatch */
+  MUON_ERR_UNSUPPORTED = -2, /* a shape or dtype outside the library's limits */
+  MUON_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+  MUON_ERR_HIP = -4          /* a HIP runtime call failed (launch error, bad stream) */
+} muon_status;
+
+typedef enum { MUON_DT_BF16 = 0, MUON_DT_F32 = 1 } muon_dtype;
+
+/* Arithmetic of the Newton-Schulz rounds.
+ *   MUON_NS_BF16:      X, A and B stored in bfloat16 (the pages' precision), products on
+ *                      bf16 matrix cores with fp32 accumulation, fp32 epilogues.
+ *   MUON_NS_F32_DEBUG: the same rounds with fp32 storage and fp32 arithmetic, to separate
+ *                      the method from its bf16 rounding. */
+typedef enum { MUON_NS_BF16 = 0, MUON_NS_F32_DEBUG = 1 } muon_precision;
+
+/* One matrix of a step.
+ *   param       rows x cols, param_dtype, updated in place (W <- W - lr*O, computed in fp32
+ *               and rounded to nearest even when param_dtype is bf16)
+ *   grad        rows x cols, grad_dtype, read only
+ *   momentum    rows x cols fp32, updated in place; zero-fill it before the first step
+ *   update_out  NULL, or rows x cols fp32 that receives O (the orthogonalised update, in the
+ *               matrix's own orientation, before the lr scaling)
+ * rows, cols and the dtypes must equal the plan's entry at the same index. */
+typedef struct {
+  void *param;
+  const void *grad;
+  float *momentum;
+  float *update_out;
+  int64_t rows;
+  int64_t cols;
+  muon_dtype param_dtype;
+  muon_dtype grad_dtype;
+} muon_matrix;
+
+/* Hyper-parameters of a step. lr, beta (momentum), nesterov and ns_steps follow the
+ * optimizer's constructor on the pages; (a, b, c) are the quintic's coefficients; eps guards
+ * the normalisation of an all-zero update. ns_steps may be 0 (O = U / (||U||_F + eps)) and
+ * is at most 64. Every float must be finite; eps >= 0. */
+typedef struct {
+  float lr;
+  float beta;
+  int nesterov;
+  int ns_steps;
+  float a, b, c;
+  float eps;
+} muon_config;
+
+/* Fills cfg with lr 0.02, beta 0.95, nesterov 1, ns_steps 5, (3.4445, -4.7750, 2.0315),
+ * eps 1e-7. A NULL cfg is ignored. */
+void muon_config_default(muon_config *cfg);
+
+/* Builds a plan for n matrices (n >= 0) of the given shapes and dtypes. The plan groups the
+ * matrices by their padded wide shape (rows and cols swapped when rows > cols, each rounded
+ * up to a multiple of 128) so that each group runs as one batch. rows and cols are in
+ * [1, 32768] with rows*cols <= 2^28. Host-only: makes no HIP call. On success *out owns the
+ * plan (release it with muon_plan_destroy); on failure *out is set to NULL. */
+int muon_plan_create(muon_plan **out, const int64_t *rows, const int64_t *cols,
+                     const muon_dtype *param_dtype, const muon_dtype *grad_dtype, int64_t n,
+                     muon_precision precision);
+
+/* Bytes of device workspace a call on this plan needs (0 for an empty plan). The workspace
+ * base must be 256-byte aligned and must not overlap any matrix buffer. Its contents need
+ * not be preserved between calls. Returns 0 for a NULL plan. */
+size_t muon_plan_workspace_size(const muon_plan *plan);
+
+/* One Muon step over mats[0..n-1]; n must equal the plan's count (n = 0 is a no-op). */
+int muon_step(muon_plan *plan, const muon_matrix *mats, int64_t n, const muon_config *cfg,
+              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The orthogonalisation alone (no momentum, no parameter update), for in[i] (rows x cols of
+ * grad_dtype) into out[i] (rows x cols of param_dtype): out = NS(in / (||in||_F + eps)) with
+ * cfg's ns_steps, a, b, c and eps; cfg's lr, beta and nesterov are ignored. This is the
+ * pages' zeropower_via_newtonschulz5 with the pre-normalisation applied. */
+int muon_newton_schulz(muon_plan *plan, const void *const *in, void *const *out, int64_t n,
+                       const muon_config *cfg, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
+
+/* Kernel timing for measurement. When enabled, every later muon_step/muon_newton_schulz
+ * records a HIP event pair around each kernel launch on the call's stream (events are
+ * created here, on the current device; the step itself still allocates nothing). Enabling
+ * resets the totals; disabling releases the events. */
+int muon_plan_set_profiling(muon_plan *plan, int enable);
+
+/* Kinds of kernel, in the order of a step. */
+typedef enum {
+  MUON_KERNEL_MOMENTUM = 0, /* momentum + Nesterov + norm partials + X0 store  */
+  MUON_KERNEL_NORM = 1,     /* per-matrix norm finish and scales              */
+  MUON_KERNEL_GRAM = 2,     /* A = s X X^T (upper tiles + mirror)             */
+  MUON_KERNEL_POLY = 3,     /* B = b A + c A A (upper tiles + mirror)         */
+  MUON_KERNEL_APPLY = 4,    /* X' = s (a X + B X)                             */
+  MUON_KERNEL_UPDATE = 5,   /* W -= lr O (and O out)                          */
+  MUON_KERNEL_KINDS = 6
+} muon_kernel_kind;
+
+/* Waits for the recorded events and writes, per kind (up to nkinds entries), the summed
+ * milliseconds and the number of launches since profiling was enabled. */
+int muon_plan_read_profile(muon_plan *plan, double *ms, int64_t *launches, int nkinds);
+
+const char *muon_status_string(int status);
+/* Message for the last failing call on this thread ("" if none). */
+const char *muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_H */

@@ -1,0 +1,80 @@
+"""Builds libmuon.so (the HIP kernels and the C ABI of include/muon.h) for gfx950 in place.
+
+    python -m orthogonalized_momentum_optimizer_amd.build
+
+Every source under csrc/ is compiled with hipcc for gfx950 only and linked into
+orthogonalized_momentum_optimizer_amd/libmuon.so. Objects go to _build/ at the repository
+root. The library links against the HIP runtime by its soname, so inside a process that has
+already loaded PyTorch's HIP runtime the library binds to that same runtime.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmuon.so")
+
+SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_gemm_f32.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-mcode-object-version=5",
+    # keep hipcc from emitting packed fp32 arithmetic
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmuon.so")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(ln for ln in (r.stderr or "").splitlines() if noise not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = []
+
+    def one(src):
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        msg = _run([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = LIB + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

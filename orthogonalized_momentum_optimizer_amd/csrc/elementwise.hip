@@ -1,0 +1,291 @@
+// HBM-bound kernels of the Muon step: the fused momentum kernel, the per-matrix norm
+// finish and the parameter update.
+//
+// Momentum and Nesterov follow the optimizer of page
+// "深入解析KellerJordan/modded-nanogpt中的训练架构与优化技术" (section
+// "Muon优化器：动量正交化技术", subsection "核心算法": standard SGD momentum, nesterov on by
+// default); the Frobenius pre-normalisation is the reading recorded in muon.h.
+//
+// Layout: every kernel works on 64x64 tiles, 256 threads, each thread owning four
+// consecutive columns of four rows (rows t/16 + 16k, columns 4*(t%16)..+3), so a wavefront
+// reads 256 contiguous bytes of fp32 per row segment. Tall matrices are transposed through
+// an LDS tile so that both the original-orientation side and the wide-form side of the
+// copy stay coalesced.
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <int DT>
+__device__ __forceinline__ float load1(const void* p, size_t i) {
+  if (DT == 0) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void load4(const void* p, size_t i, float v[4]) {
+  if (DT == 0) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    v[0] = bf16_bits_to_f32(w.x & 0xffffu);
+    v[1] = bf16_bits_to_f32(w.x >> 16);
+    v[2] = bf16_bits_to_f32(w.y & 0xffffu);
+    v[3] = bf16_bits_to_f32(w.y >> 16);
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store1(void* p, size_t i, float v) {
+  if (DT == 0) static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else static_cast<float*>(p)[i] = v;
+}
+
+template <int DT>
+__device__ __forceinline__ void store4(void* p, size_t i, const float v[4]) {
+  if (DT == 0) {
+    uint2 w;
+    w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One 64x64 tile of the padded wide form X (mp x np) per block, matrix q = blockIdx.y.
+// Momentum (in place), U, the tile's sum of U^2, and X0 = U stored in the wide form; padding
+// positions of X0 receive zeros. GDT: grad dtype, XDT: X dtype (0 bf16, 1 f32).
+template <int GDT, int XDT>
+__global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
+  __shared__ float tile[kTile][kTile + 1];
+  __shared__ float red[4];
+  const int q = blockIdx.y;
+  const int t = threadIdx.x;
+  const int tiles_n = L.np / kTile;
+  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;  // wide tile coordinates
+  const int r0 = L.tall ? tj * kTile : ti * kTile;                  // original-orientation origin
+  const int c0 = L.tall ? ti * kTile : tj * kTile;
+  const void* g = L.in[q];
+  float* mom = L.mom[q];
+  void* x = static_cast<char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
+  const float beta = L.beta;
+  const int lc = 4 * (t & 15);
+  float ss = 0.f;
+
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int lr = (t >> 4) + 16 * k;
+    const int r = r0 + lr, c = c0 + lc;
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < L.rows) {
+      const size_t base = (size_t)r * L.cols + c;
+      if (L.vec) {
+        if (c < L.cols) {
+          float gv[4];
+          load4<GDT>(g, base, gv);
+          if (mom) {
+            float4 mv = *reinterpret_cast<const float4*>(mom + base);
+            float m4[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              m4[e] = fmaf(beta, m4[e], gv[e]);
+              u[e] = L.nesterov ? fmaf(beta, m4[e], gv[e]) : m4[e];
+            }
+            *reinterpret_cast<float4*>(mom + base) = make_float4(m4[0], m4[1], m4[2], m4[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = gv[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c + e < L.cols) {
+            const float gv = load1<GDT>(g, base + e);
+            if (mom) {
+              const float m = fmaf(beta, mom[base + e], gv);
+              mom[base + e] = m;
+              u[e] = L.nesterov ? fmaf(beta, m, gv) : m;
+            } else {
+              u[e] = gv;
+            }
+          }
+        }
+      }
+    }
+    ss += (u[0] * u[0] + u[1] * u[1]) + (u[2] * u[2] + u[3] * u[3]);
+    if (!L.tall) {
+      store4<XDT>(x, (size_t)r * L.np + c, u);  // wide (i, j) = (r, c); r < mp, c < np
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[lr][lc + e] = u[e];
+    }
+  }
+
+  if (L.tall) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int a = (t >> 4) + 16 * k;  // wide row (original column) within the tile
+      const int b = 4 * (t & 15);       // wide column (original row) within the tile
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[b + e][a];
+      store4<XDT>(x, (size_t)(c0 + a) * L.np + (r0 + b), v);
+    }
+  }
+
+  ss = wave_sum(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  if (t == 0) {
+    const int tiles = (L.mp / kTile) * tiles_n;
+    L.partials[(size_t)q * tiles + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  }
+}
+
+// One block per matrix: nu = sqrt(sum of tile partials) in double, in a fixed order.
+__global__ __launch_bounds__(256) void norm_kernel(const float* partials, int tiles,
+                                                   float* scales, float eps) {
+  __shared__ double red[4];
+  const int q = blockIdx.x, t = threadIdx.x;
+  const float* p = partials + (size_t)q * tiles;
+  double s = 0.0;
+  for (int i = t; i < tiles; i += 256) s += (double)p[i];
+  s = wave_sum(s);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) {
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const double nu = sqrt(tot);
+    const double s1 = 1.0 / (nu + (double)eps);
+    scales[4 * q + 0] = (float)s1;
+    scales[4 * q + 1] = (float)(s1 * s1);
+    scales[4 * q + 2] = (float)nu;
+    scales[4 * q + 3] = 0.f;
+  }
+}
+
+// One 64x64 tile of the original orientation per block, matrix q = blockIdx.y:
+// O = X (or X^T for tall matrices) [* s1], W <- W - lr * O, optional O output.
+// PDT: param dtype, ODT: dtype of the O output, XDT: X dtype.
+template <int PDT, int ODT, int XDT>
+__global__ __launch_bounds__(256) void update_kernel(ElemLaunch L) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int q = blockIdx.y;
+  const int t = threadIdx.x;
+  const int tiles_c = (L.cols + kTile - 1) / kTile;
+  const int r0 = (blockIdx.x / tiles_c) * kTile, c0 = (blockIdx.x % tiles_c) * kTile;
+  const void* x = static_cast<const char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
+  void* w = L.param[q];
+  void* o = L.out[q];
+  const float s = L.apply_scale ? L.scales[4 * q] : 1.f;
+  const float lr = L.lr;
+
+  if (L.tall) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int a = (t >> 4) + 16 * k, b = 4 * (t & 15);
+      float v[4];
+      load4<XDT>(x, (size_t)(c0 + a) * L.np + (r0 + b), v);  // within the padded buffer
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[a][b + e] = v[e];
+    }
+    __syncthreads();
+  }
+
+  const int lc = 4 * (t & 15);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int lr_ = (t >> 4) + 16 * k;
+    const int r = r0 + lr_, c = c0 + lc;
+    if (r >= L.rows) continue;
+    float ov[4];
+    if (L.tall) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = tile[lc + e][lr_];
+    } else {
+      load4<XDT>(x, (size_t)r * L.np + c, ov);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] *= s;
+    const size_t base = (size_t)r * L.cols + c;
+    if (L.vec) {
+      if (c >= L.cols) continue;
+      if (w) {
+        float wv[4];
+        load4<PDT>(w, base, wv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = fmaf(-lr, ov[e], wv[e]);
+        store4<PDT>(w, base, wv);
+      }
+      if (o) store4<ODT>(o, base, ov);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c + e >= L.cols) break;
+        if (w) store1<PDT>(w, base + e, fmaf(-lr, ov[e], load1<PDT>(w, base + e)));
+        if (o) store1<ODT>(o, base + e, ov[e]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStream_t s) {
+  const dim3 grid((L.mp / kTile) * (L.np / kTile), L.count), block(256);
+  if (grad_dt == 0 && !x_f32) hipLaunchKernelGGL((momentum_kernel<0, 0>), grid, block, 0, s, L);
+  else if (grad_dt == 0) hipLaunchKernelGGL((momentum_kernel<0, 1>), grid, block, 0, s, L);
+  else if (!x_f32) hipLaunchKernelGGL((momentum_kernel<1, 0>), grid, block, 0, s, L);
+  else hipLaunchKernelGGL((momentum_kernel<1, 1>), grid, block, 0, s, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const float* partials, int tiles, float* scales, int count, float eps,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(count), dim3(256), 0, s, partials, tiles, scales, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_dt, int x_f32,
+                         hipStream_t s) {
+  const int tiles = ((L.rows + kTile - 1) / kTile) * ((L.cols + kTile - 1) / kTile);
+  const dim3 grid(tiles, L.count), block(256);
+  const int code = param_dt * 4 + out_dt * 2 + x_f32;
+  switch (code) {
+    case 0: hipLaunchKernelGGL((update_kernel<0, 0, 0>), grid, block, 0, s, L); break;
+    case 1: hipLaunchKernelGGL((update_kernel<0, 0, 1>), grid, block, 0, s, L); break;
+    case 2: hipLaunchKernelGGL((update_kernel<0, 1, 0>), grid, block, 0, s, L); break;
+    case 3: hipLaunchKernelGGL((update_kernel<0, 1, 1>), grid, block, 0, s, L); break;
+    case 4: hipLaunchKernelGGL((update_kernel<1, 0, 0>), grid, block, 0, s, L); break;
+    case 5: hipLaunchKernelGGL((update_kernel<1, 0, 1>), grid, block, 0, s, L); break;
+    case 6: hipLaunchKernelGGL((update_kernel<1, 1, 0>), grid, block, 0, s, L); break;
+    default: hipLaunchKernelGGL((update_kernel<1, 1, 1>), grid, block, 0, s, L); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muon

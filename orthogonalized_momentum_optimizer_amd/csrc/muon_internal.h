@@ -1,0 +1,63 @@
+// Internal interfaces between the host plan (plan.hip) and the kernel launchers.
+// Every launcher enqueues on `stream`, returns the hipError_t of the launch, and assumes the
+// host has validated shapes, pointers and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kPad = 128;        // wide shapes are padded to multiples of this
+constexpr int kTile = 64;        // elementwise kernels work on 64x64 tiles
+constexpr int kMaxPerLaunch = 48;  // matrices per elementwise launch (pointers travel by value)
+
+// Elementwise launch over up to kMaxPerLaunch matrices of one shape and dtype pair.
+// Matrix q of the launch owns slot (slot0 + q) of its group's workspace buffers.
+struct ElemLaunch {
+  const void* in[kMaxPerLaunch];   // K1: grad;  update: unused
+  float* mom[kMaxPerLaunch];       // K1: momentum (nullptr = no momentum phase)
+  void* param[kMaxPerLaunch];      // update: W (nullptr = write O only)
+  void* out[kMaxPerLaunch];        // update: O destination (nullptr = none)
+  int count;
+  int rows, cols;                  // original orientation
+  int tall;                        // rows > cols: the wide form is the transpose
+  int mp, np;                      // padded wide shape (X is mp x np)
+  int vec;                         // cols % 4 == 0: 4-wide vector access along rows
+  void* x;                         // X buffer of slot0 (bf16 or f32), slot stride mp*np
+  float* partials;                 // K1: per-tile sums of squares of slot0
+  const float* scales;             // per-slot {s1, s2, nu, 0} of slot0
+  float beta;
+  int nesterov;
+  float lr;
+  int apply_scale;                 // update: multiply X by s1 (ns_steps == 0)
+};
+
+// dtype codes: 0 = bf16, 1 = f32 (match muon_dtype)
+hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStream_t s);
+hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_param_dt, int x_f32,
+                         hipStream_t s);
+// Per-matrix norm finish: scales[4*i] = 1/(nu+eps), [4*i+1] = that squared, [4*i+2] = nu.
+hipError_t launch_norm(const float* partials, int tiles_per_mat, float* scales, int count,
+                       float eps, hipStream_t s);
+
+// One batched Newton-Schulz product over a group of `batch` padded mp x np matrices.
+struct NsGroup {
+  void* x_in;          // X, batch x mp x np
+  void* x_out;         // X', batch x mp x np
+  void* a;             // A, batch x mp x mp
+  void* b;             // B, batch x mp x mp
+  const float* scales; // per matrix {s1, s2, nu, 0}; used when first != 0
+  int batch, mp, np;
+  int first;           // first round: fold the 1/nu normalisation into the epilogues
+};
+// bf16 storage, bf16 matrix cores with fp32 accumulation (ns_gemm_bf16.hip)
+hipError_t launch_gram_bf16(const NsGroup& g, hipStream_t s);                    // A = s2 X X^T
+hipError_t launch_poly_bf16(const NsGroup& g, float b, float c, hipStream_t s);  // B = bA + cAA
+hipError_t launch_apply_bf16(const NsGroup& g, float a, hipStream_t s);          // X' = s1(aX+BX)
+// fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip)
+hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);
+hipError_t launch_poly_f32(const NsGroup& g, float b, float c, hipStream_t s);
+hipError_t launch_apply_f32(const NsGroup& g, float a, hipStream_t s);
+
+}  // namespace muon

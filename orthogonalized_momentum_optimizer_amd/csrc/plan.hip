@@ -1,0 +1,552 @@
+// Host side of the C ABI declared in include/muon.h: plans, validation, workspace layout
+// and the order of launches of one Muon step.
+//
+// The step's three phases (momentum, Newton-Schulz orthogonalisation, parameter update)
+// follow page "深入解析KellerJordan/modded-nanogpt中的训练架构与优化技术", section
+// "Muon优化器：动量正交化技术"; the grouping of matrices by size into batches follows the
+// same page's section "训练优化技巧" / "分布式训练优化" (processing grouped by parameter
+// size). Here a group is every matrix with the same padded wide shape, so each product of
+// a Newton-Schulz round is one batched launch per group.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int pad_up(int64_t x) { return (int)((x + kPad - 1) / kPad * kPad); }
+size_t dt_size(muon_dtype d) { return d == MUON_DT_BF16 ? 2 : 4; }
+
+struct LaunchSet {  // matrices of one shape and dtype pair, contiguous slots of a group
+  int group = 0, slot0 = 0;
+  int rows = 0, cols = 0;
+  muon_dtype pdt = MUON_DT_BF16, gdt = MUON_DT_BF16;
+  std::vector<int> mats;  // matrix indices, in slot order
+};
+
+struct Group {
+  int mp = 0, np = 0, count = 0, tiles64 = 0;
+  size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0, off_scales = 0;
+  std::vector<int> sets;
+};
+
+struct Range {
+  uintptr_t lo, hi;
+  bool writable;
+};
+
+}  // namespace
+
+struct muon_plan {
+  int64_t n = 0;
+  muon_precision prec = MUON_NS_BF16;
+  std::vector<int64_t> rows, cols;
+  std::vector<muon_dtype> pdt, gdt;
+  std::vector<Group> groups;
+  std::vector<LaunchSet> sets;
+  size_t ws_bytes = 0;
+  // last argument set that passed the overlap check
+  std::vector<muon_matrix> checked_mats;
+  std::vector<const void*> checked_ptrs;
+  const void* checked_ws = nullptr;
+  // profiling
+  bool prof = false;
+  std::vector<hipEvent_t> ev;  // pairs (start, stop)
+  std::vector<int> ev_kind;    // kind of each recorded pair of the pending call
+  int ev_used = 0;             // pairs recorded by the pending call
+  double prof_ms[MUON_KERNEL_KINDS] = {};
+  int64_t prof_launches[MUON_KERNEL_KINDS] = {};
+};
+
+namespace {
+
+bool finite(float x) { return std::isfinite(x); }
+
+int check_cfg(const muon_config* cfg, bool momentum) {
+  if (!cfg) return fail(MUON_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->ns_steps < 0 || cfg->ns_steps > 64)
+    return fail(MUON_ERR_INVALID_ARG, "ns_steps = %d outside [0, 64]", cfg->ns_steps);
+  if (!finite(cfg->a) || !finite(cfg->b) || !finite(cfg->c))
+    return fail(MUON_ERR_INVALID_ARG, "coefficients (a, b, c) must be finite");
+  if (!finite(cfg->eps) || cfg->eps < 0.f)
+    return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (momentum && (!finite(cfg->lr) || !finite(cfg->beta)))
+    return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
+  return MUON_OK;
+}
+
+int check_workspace(const muon_plan* p, const void* ws, size_t bytes) {
+  if (p->ws_bytes == 0) return MUON_OK;
+  if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p->ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(MUON_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+  if (bytes < p->ws_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, p->ws_bytes);
+  return MUON_OK;
+}
+
+// Any overlap that involves a buffer the call writes is an error.
+int check_overlaps(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  uintptr_t max_any = 0, max_w = 0;
+  for (const Range& r : rs) {
+    if (r.lo < max_w || (r.writable && r.lo < max_any))
+      return fail(MUON_ERR_INVALID_ARG,
+                  "buffer [%p, %p) overlaps another buffer of the call, and one of them is "
+                  "written", (void*)r.lo, (void*)r.hi);
+    max_any = std::max(max_any, r.hi);
+    if (r.writable) max_w = std::max(max_w, r.hi);
+  }
+  return MUON_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ---- profiling -------------------------------------------------------------------------
+
+void prof_collect(muon_plan* p) {
+  if (!p->prof || p->ev_used == 0) return;
+  (void)hipEventSynchronize(p->ev[2 * p->ev_used - 1]);
+  for (int i = 0; i < p->ev_used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p->ev[2 * i], p->ev[2 * i + 1]) == hipSuccess) {
+      p->prof_ms[p->ev_kind[i]] += ms;
+      p->prof_launches[p->ev_kind[i]] += 1;
+    }
+  }
+  p->ev_used = 0;
+}
+
+struct Launcher {
+  muon_plan* p;
+  hipStream_t s;
+  int status = MUON_OK;
+
+  template <class F>
+  void run(int kind, const char* what, F&& f) {
+    if (status != MUON_OK) return;
+    const bool timed = p->prof && p->ev_used < (int)p->ev.size() / 2;
+    if (timed) (void)hipEventRecord(p->ev[2 * p->ev_used], s);
+    const hipError_t e = f();
+    if (e != hipSuccess) {
+      status = fail(MUON_ERR_HIP, "launch of %s failed: %s", what, hipGetErrorString(e));
+      return;
+    }
+    if (timed) {
+      (void)hipEventRecord(p->ev[2 * p->ev_used + 1], s);
+      p->ev_kind[p->ev_used] = kind;
+      ++p->ev_used;
+    }
+  }
+};
+
+// ---- the step ----------------------------------------------------------------------------
+
+// grads: per matrix input (grad or NS input); moms: momentum (nullable array = no momentum
+// phase); params: W (nullable array = no update); outs: O destination (nullable entries);
+// out_param_dtype: O is written in the param dtype (else fp32).
+int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* const* params,
+            void* const* outs, bool out_param_dtype, const muon_config* cfg, void* ws,
+            hipStream_t stream) {
+  prof_collect(p);
+  Launcher L{p, stream};
+  const bool f32 = p->prec == MUON_NS_F32_DEBUG;
+  const size_t esz = f32 ? 4 : 2;
+  char* base = static_cast<char*>(ws);
+
+  for (size_t gi = 0; gi < p->groups.size(); ++gi) {
+    const Group& G = p->groups[gi];
+    char* x0 = base + G.off_x0;
+    char* x1 = base + G.off_x1;
+    float* part = reinterpret_cast<float*>(base + G.off_part);
+    float* scales = reinterpret_cast<float*>(base + G.off_scales);
+    const size_t xslot = (size_t)G.mp * G.np * esz;
+
+    // phase 1: momentum, norm partials, X0
+    for (int si : G.sets) {
+      const LaunchSet& S = p->sets[si];
+      for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
+        ElemLaunch E{};
+        E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
+        for (int q = 0; q < E.count; ++q) {
+          const int m = S.mats[q0 + q];
+          E.in[q] = grads[m];
+          E.mom[q] = moms ? moms[m] : nullptr;
+        }
+        E.rows = S.rows;
+        E.cols = S.cols;
+        E.tall = S.rows > S.cols;
+        E.mp = G.mp;
+        E.np = G.np;
+        E.vec = (S.cols % 4) == 0;
+        const int slot = S.slot0 + (int)q0;
+        E.x = x0 + (size_t)slot * xslot;
+        E.partials = part + (size_t)slot * G.tiles64;
+        E.beta = cfg->beta;
+        E.nesterov = cfg->nesterov ? 1 : 0;
+        L.run(MUON_KERNEL_MOMENTUM, "momentum",
+              [&] { return launch_momentum(E, S.gdt == MUON_DT_F32, f32, stream); });
+      }
+    }
+    L.run(MUON_KERNEL_NORM, "norm",
+          [&] { return launch_norm(part, G.tiles64, scales, G.count, cfg->eps, stream); });
+
+    // phase 2: Newton-Schulz rounds, ping-pong between x0 and x1
+    NsGroup N{};
+    N.a = base + G.off_a;
+    N.b = base + G.off_b;
+    N.scales = scales;
+    N.batch = G.count;
+    N.mp = G.mp;
+    N.np = G.np;
+    char* xin = x0;
+    char* xout = x1;
+    for (int r = 0; r < cfg->ns_steps; ++r) {
+      N.x_in = xin;
+      N.x_out = xout;
+      N.first = r == 0;
+      L.run(MUON_KERNEL_GRAM, "gram",
+            [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(N, stream); });
+      L.run(MUON_KERNEL_POLY, "poly", [&] {
+        return f32 ? launch_poly_f32(N, cfg->b, cfg->c, stream)
+                   : launch_poly_bf16(N, cfg->b, cfg->c, stream);
+      });
+      L.run(MUON_KERNEL_APPLY, "apply", [&] {
+        return f32 ? launch_apply_f32(N, cfg->a, stream) : launch_apply_bf16(N, cfg->a, stream);
+      });
+      std::swap(xin, xout);
+    }
+
+    // phase 3: parameter update (and O output)
+    for (int si : G.sets) {
+      const LaunchSet& S = p->sets[si];
+      for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
+        ElemLaunch E{};
+        E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
+        for (int q = 0; q < E.count; ++q) {
+          const int m = S.mats[q0 + q];
+          E.param[q] = params ? params[m] : nullptr;
+          E.out[q] = outs ? outs[m] : nullptr;
+        }
+        E.rows = S.rows;
+        E.cols = S.cols;
+        E.tall = S.rows > S.cols;
+        E.mp = G.mp;
+        E.np = G.np;
+        E.vec = (S.cols % 4) == 0;
+        const int slot = S.slot0 + (int)q0;
+        E.x = xin + (size_t)slot * xslot;
+        E.scales = scales + 4 * (size_t)slot;
+        E.apply_scale = cfg->ns_steps == 0;
+        E.lr = cfg->lr;
+        const int out_dt = out_param_dtype ? (S.pdt == MUON_DT_F32) : 1;
+        L.run(MUON_KERNEL_UPDATE, "update",
+              [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
+      }
+    }
+    if (L.status != MUON_OK) return L.status;
+  }
+  return L.status;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_config_default(muon_config* cfg) {
+  if (!cfg) return;
+  cfg->lr = 0.02f;
+  cfg->beta = 0.95f;
+  cfg->nesterov = 1;
+  cfg->ns_steps = 5;
+  cfg->a = 3.4445f;
+  cfg->b = -4.7750f;
+  cfg->c = 2.0315f;
+  cfg->eps = 1e-7f;
+}
+
+int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
+                     const muon_dtype* param_dtype, const muon_dtype* grad_dtype, int64_t n,
+                     muon_precision precision) {
+  g_last_error.clear();
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
+  if (n > 0 && (!rows || !cols || !param_dtype || !grad_dtype))
+    return fail(MUON_ERR_INVALID_ARG, "rows, cols, param_dtype and grad_dtype must be non-NULL");
+  if (precision != MUON_NS_BF16 && precision != MUON_NS_F32_DEBUG)
+    return fail(MUON_ERR_INVALID_ARG, "unknown precision %d", (int)precision);
+  for (int64_t i = 0; i < n; ++i) {
+    if (rows[i] < 1 || cols[i] < 1)
+      return fail(MUON_ERR_INVALID_ARG, "matrix %lld has shape %lld x %lld", (long long)i,
+                  (long long)rows[i], (long long)cols[i]);
+    if (rows[i] > 32768 || cols[i] > 32768 || rows[i] * cols[i] > (int64_t(1) << 28))
+      return fail(MUON_ERR_UNSUPPORTED, "matrix %lld: %lld x %lld exceeds the limits",
+                  (long long)i, (long long)rows[i], (long long)cols[i]);
+    for (muon_dtype d : {param_dtype[i], grad_dtype[i]})
+      if (d != MUON_DT_BF16 && d != MUON_DT_F32)
+        return fail(MUON_ERR_INVALID_ARG, "matrix %lld: unknown dtype %d", (long long)i, (int)d);
+  }
+
+  muon_plan* p = new (std::nothrow) muon_plan();
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "out of host memory");
+  p->n = n;
+  p->prec = precision;
+  p->rows.assign(rows, rows + n);
+  p->cols.assign(cols, cols + n);
+  p->pdt.assign(param_dtype, param_dtype + n);
+  p->gdt.assign(grad_dtype, grad_dtype + n);
+
+  // groups by padded wide shape, launch sets by (rows, cols, dtypes), in order of appearance
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t m = std::min(rows[i], cols[i]), w = std::max(rows[i], cols[i]);
+    const int mp = pad_up(m), np = pad_up(w);
+    int g = -1;
+    for (size_t k = 0; k < p->groups.size(); ++k)
+      if (p->groups[k].mp == mp && p->groups[k].np == np) g = (int)k;
+    if (g < 0) {
+      g = (int)p->groups.size();
+      Group G;
+      G.mp = mp;
+      G.np = np;
+      G.tiles64 = (mp / kTile) * (np / kTile);
+      p->groups.push_back(G);
+    }
+    int s = -1;
+    for (int k : p->groups[g].sets) {
+      const LaunchSet& S = p->sets[k];
+      if (S.rows == rows[i] && S.cols == cols[i] && S.pdt == param_dtype[i] &&
+          S.gdt == grad_dtype[i])
+        s = k;
+    }
+    if (s < 0) {
+      s = (int)p->sets.size();
+      LaunchSet S;
+      S.group = g;
+      S.rows = (int)rows[i];
+      S.cols = (int)cols[i];
+      S.pdt = param_dtype[i];
+      S.gdt = grad_dtype[i];
+      p->sets.push_back(S);
+      p->groups[g].sets.push_back(s);
+    }
+    p->sets[s].mats.push_back((int)i);
+  }
+
+  const size_t esz = precision == MUON_NS_F32_DEBUG ? 4 : 2;
+  size_t off = 0;
+  for (Group& G : p->groups) {
+    int slot = 0;
+    for (int s : G.sets) {
+      p->sets[s].slot0 = slot;
+      slot += (int)p->sets[s].mats.size();
+    }
+    G.count = slot;
+    const size_t xs = (size_t)G.count * G.mp * G.np * esz;
+    const size_t as = (size_t)G.count * G.mp * G.mp * esz;
+    G.off_x0 = off; off = align256(off + xs);
+    G.off_x1 = off; off = align256(off + xs);
+    G.off_a = off; off = align256(off + as);
+    G.off_b = off; off = align256(off + as);
+    G.off_part = off; off = align256(off + (size_t)G.count * G.tiles64 * 4);
+    G.off_scales = off; off = align256(off + (size_t)G.count * 16);
+  }
+  p->ws_bytes = off;
+  *out = p;
+  return MUON_OK;
+}
+
+size_t muon_plan_workspace_size(const muon_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_config* cfg,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (n != plan->n)
+    return fail(MUON_ERR_INVALID_ARG, "n = %lld but the plan has %lld matrices", (long long)n,
+                (long long)plan->n);
+  if (int st = check_cfg(cfg, true)) return st;
+  if (n == 0) return MUON_OK;
+  if (!mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+  if (int st = check_workspace(plan, workspace, workspace_bytes)) return st;
+
+  const bool same = plan->checked_ws == workspace && plan->checked_mats.size() == (size_t)n &&
+                    std::memcmp(plan->checked_mats.data(), mats, sizeof(muon_matrix) * n) == 0;
+  if (!same) {
+    std::vector<Range> rs;
+    rs.reserve(4 * n + 1);
+    for (int64_t i = 0; i < n; ++i) {
+      const muon_matrix& M = mats[i];
+      if (M.rows != plan->rows[i] || M.cols != plan->cols[i] ||
+          M.param_dtype != plan->pdt[i] || M.grad_dtype != plan->gdt[i])
+        return fail(MUON_ERR_INVALID_ARG,
+                    "matrix %lld: shape/dtype (%lld x %lld, %d, %d) differ from the plan's",
+                    (long long)i, (long long)M.rows, (long long)M.cols, (int)M.param_dtype,
+                    (int)M.grad_dtype);
+      if (!M.param || !M.grad || !M.momentum)
+        return fail(MUON_ERR_INVALID_ARG, "matrix %lld: param, grad and momentum must be non-NULL",
+                    (long long)i);
+      if (!aligned16(M.param) || !aligned16(M.grad) || !aligned16(M.momentum) ||
+          (M.update_out && !aligned16(M.update_out)))
+        return fail(MUON_ERR_INVALID_ARG, "matrix %lld: buffers must be 16-byte aligned",
+                    (long long)i);
+      const size_t elems = (size_t)M.rows * M.cols;
+      auto add = [&](const void* ptr, size_t bytes, bool w) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+        rs.push_back({lo, lo + bytes, w});
+      };
+      add(M.param, elems * dt_size(M.param_dtype), true);
+      add(M.grad, elems * dt_size(M.grad_dtype), false);
+      add(M.momentum, elems * 4, true);
+      if (M.update_out) add(M.update_out, elems * 4, true);
+    }
+    if (plan->ws_bytes) rs.push_back({reinterpret_cast<uintptr_t>(workspace),
+                                      reinterpret_cast<uintptr_t>(workspace) + plan->ws_bytes,
+                                      true});
+    if (int st = check_overlaps(rs)) return st;
+    plan->checked_mats.assign(mats, mats + n);
+    plan->checked_ws = workspace;
+  }
+
+  std::vector<const void*> grads(n);
+  std::vector<float*> moms(n);
+  std::vector<void*> params(n), outs(n);
+  for (int64_t i = 0; i < n; ++i) {
+    grads[i] = mats[i].grad;
+    moms[i] = mats[i].momentum;
+    params[i] = mats[i].param;
+    outs[i] = mats[i].update_out;
+  }
+  return enqueue(plan, grads.data(), moms.data(), params.data(), outs.data(), false, cfg,
+                 workspace, stream);
+}
+
+int muon_newton_schulz(muon_plan* plan, const void* const* in, void* const* out, int64_t n,
+                       const muon_config* cfg, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (n != plan->n)
+    return fail(MUON_ERR_INVALID_ARG, "n = %lld but the plan has %lld matrices", (long long)n,
+                (long long)plan->n);
+  if (int st = check_cfg(cfg, false)) return st;
+  if (n == 0) return MUON_OK;
+  if (!in || !out) return fail(MUON_ERR_INVALID_ARG, "in and out must be non-NULL");
+  if (int st = check_workspace(plan, workspace, workspace_bytes)) return st;
+  std::vector<Range> rs;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!in[i] || !out[i])
+      return fail(MUON_ERR_INVALID_ARG, "matrix %lld: in and out must be non-NULL", (long long)i);
+    if (!aligned16(in[i]) || !aligned16(out[i]))
+      return fail(MUON_ERR_INVALID_ARG, "matrix %lld: buffers must be 16-byte aligned",
+                  (long long)i);
+    const size_t elems = (size_t)plan->rows[i] * plan->cols[i];
+    const uintptr_t a = reinterpret_cast<uintptr_t>(in[i]), b = reinterpret_cast<uintptr_t>(out[i]);
+    rs.push_back({a, a + elems * dt_size(plan->gdt[i]), false});
+    rs.push_back({b, b + elems * dt_size(plan->pdt[i]), true});
+  }
+  if (plan->ws_bytes)
+    rs.push_back({reinterpret_cast<uintptr_t>(workspace),
+                  reinterpret_cast<uintptr_t>(workspace) + plan->ws_bytes, true});
+  if (int st = check_overlaps(rs)) return st;
+  return enqueue(plan, in, nullptr, nullptr, out, true, cfg, workspace, stream);
+}
+
+void muon_plan_destroy(muon_plan* plan) {
+  if (!plan) return;
+  if (plan->prof) {
+    prof_collect(plan);
+    for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
+  }
+  delete plan;
+}
+
+int muon_plan_set_profiling(muon_plan* plan, int enable) {
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->prof) {
+    prof_collect(plan);
+    for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
+    plan->ev.clear();
+    plan->ev_kind.clear();
+    plan->prof = false;
+  }
+  std::fill(std::begin(plan->prof_ms), std::end(plan->prof_ms), 0.0);
+  std::fill(std::begin(plan->prof_launches), std::end(plan->prof_launches), 0);
+  if (!enable) return MUON_OK;
+  // launches of one call with the largest ns_steps: per group 2 elementwise passes, the norm
+  // and 3 products per round
+  size_t pairs = 0;
+  for (const Group& G : plan->groups) {
+    size_t chunks = 0;
+    for (int s : G.sets) chunks += (plan->sets[s].mats.size() + kMaxPerLaunch - 1) / kMaxPerLaunch;
+    pairs += 2 * chunks + 1 + 3 * 64;
+  }
+  plan->ev.resize(2 * pairs);
+  plan->ev_kind.assign(pairs, 0);
+  for (size_t i = 0; i < plan->ev.size(); ++i) {
+    const hipError_t e = hipEventCreate(&plan->ev[i]);
+    if (e != hipSuccess) {
+      for (size_t k = 0; k < i; ++k) (void)hipEventDestroy(plan->ev[k]);
+      plan->ev.clear();
+      return fail(MUON_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(e));
+    }
+  }
+  plan->ev_used = 0;
+  plan->prof = true;
+  return MUON_OK;
+}
+
+int muon_plan_read_profile(muon_plan* plan, double* ms, int64_t* launches, int nkinds) {
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (nkinds < 0 || (nkinds > 0 && (!ms || !launches)))
+    return fail(MUON_ERR_INVALID_ARG, "ms and launches must hold nkinds entries");
+  prof_collect(plan);
+  for (int k = 0; k < nkinds && k < MUON_KERNEL_KINDS; ++k) {
+    ms[k] = plan->prof_ms[k];
+    launches[k] = plan->prof_launches[k];
+  }
+  for (int k = MUON_KERNEL_KINDS; k < nkinds; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  return MUON_OK;
+}
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    default: return "unknown muon status";
+  }
+}
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

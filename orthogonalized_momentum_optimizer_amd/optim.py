@@ -1,0 +1,203 @@
+"""PyTorch-facing wrappers of the C ABI: a plan holder, the Newton-Schulz function and the
+``Muon`` optimizer.
+
+The optimizer mirrors the constructor of page
+"深入解析KellerJordan/modded-nanogpt中的训练架构与优化技术" (section
+"Muon优化器：动量正交化技术", subsection "核心算法"): ``Muon(params, lr=0.02,
+momentum=0.95, nesterov=True, ns_steps=5)``, with per-parameter "update buffers" (the
+fp32 momentum). PyTorch supplies device memory and the current stream; the step itself
+runs entirely in libmuon.so.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.bfloat16: L.MUON_DT_BF16, torch.float32: L.MUON_DT_F32}
+_PREC = {"bf16": L.MUON_NS_BF16, "f32": L.MUON_NS_F32_DEBUG}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}: the library takes bfloat16 or float32")
+    return _DT[dt]
+
+
+def make_config(lr=0.02, beta=0.95, nesterov=True, ns_steps=5, abc=(3.4445, -4.7750, 2.0315),
+                eps=1e-7) -> L.muon_config:
+    cfg = L.muon_config_default()
+    cfg.lr, cfg.beta, cfg.nesterov, cfg.ns_steps = lr, beta, int(bool(nesterov)), int(ns_steps)
+    cfg.a, cfg.b, cfg.c = abc
+    cfg.eps = eps
+    return cfg
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class MuonPlan:
+    """A plan of the library for a fixed list of matrix shapes and dtypes, with its device
+    workspace (allocated once here, never inside a step)."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], param_dtypes: Sequence[torch.dtype],
+                 grad_dtypes: Sequence[torch.dtype], precision: str = "bf16",
+                 device: Optional[torch.device] = None):
+        self.shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.pdt = [dtype_code(d) for d in param_dtypes]
+        self.gdt = [dtype_code(d) for d in grad_dtypes]
+        self.precision = precision
+        self.handle = L.muon_plan_create([s[0] for s in self.shapes], [s[1] for s in self.shapes],
+                                         self.pdt, self.gdt, _PREC[precision])
+        self.ws_bytes = L.muon_plan_workspace_size(self.handle)
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        assert self.workspace.data_ptr() % 256 == 0
+        self._mats = None
+        self._mats_key = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            L.muon_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _matrices(self, params, grads, moms, outs):
+        n = len(self.shapes)
+        outs = outs if outs is not None else [None] * n
+        key = tuple((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0)
+                    for p, g, m, o in zip(params, grads, moms, outs))
+        if key != self._mats_key:
+            ents = []
+            for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
+                r, c = self.shapes[i]
+                for t in (p, g, m) + ((o,) if o is not None else ()):
+                    if tuple(t.shape) != (r, c) or not t.is_contiguous() or not t.is_cuda:
+                        raise ValueError(f"matrix {i}: tensors must be contiguous CUDA "
+                                         f"{r}x{c} (got {tuple(t.shape)})")
+                if m.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
+                    raise TypeError(f"matrix {i}: momentum and update_out must be float32")
+                ents.append((p.data_ptr(), g.data_ptr(), m.data_ptr(),
+                             o.data_ptr() if o is not None else None, r, c,
+                             dtype_code(p.dtype), dtype_code(g.dtype)))
+            self._mats = L.make_matrices(ents)
+            self._mats_key = key
+        return self._mats
+
+    def set_profiling(self, enable: bool):
+        L.muon_plan_set_profiling(self.handle, enable)
+
+    def read_profile(self) -> dict:
+        return L.muon_plan_read_profile(self.handle)
+
+    def step(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+             moms: Sequence[torch.Tensor], cfg: L.muon_config,
+             outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> None:
+        n = len(self.shapes)
+        if not (len(params) == len(grads) == len(moms) == n):
+            raise ValueError(f"expected {n} params, grads and momentum buffers")
+        mats = self._matrices(params, grads, moms, outs) if n else None
+        L.muon_step(self.handle, mats, n, cfg, self.workspace.data_ptr(), self.ws_bytes,
+                    _stream_handle(stream))
+
+    def newton_schulz(self, inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor],
+                      cfg: L.muon_config, stream: Optional[torch.cuda.Stream] = None) -> None:
+        n = len(self.shapes)
+        if not (len(inputs) == len(outputs) == n):
+            raise ValueError(f"expected {n} inputs and outputs")
+        for i, (x, y) in enumerate(zip(inputs, outputs)):
+            if (tuple(x.shape) != self.shapes[i] or tuple(y.shape) != self.shapes[i]
+                    or not x.is_contiguous() or not y.is_contiguous()):
+                raise ValueError(f"matrix {i}: contiguous {self.shapes[i]} tensors expected")
+            if dtype_code(x.dtype) != self.gdt[i] or dtype_code(y.dtype) != self.pdt[i]:
+                raise TypeError(f"matrix {i}: dtypes differ from the plan's")
+        L.muon_newton_schulz(self.handle, [x.data_ptr() for x in inputs],
+                             [y.data_ptr() for y in outputs], cfg, self.workspace.data_ptr(),
+                             self.ws_bytes, _stream_handle(stream))
+
+
+def zeropower_via_newtonschulz5(G: torch.Tensor, steps: int = 5, precision: str = "bf16",
+                                out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """NS(G / (||G||_F + eps)) for one 2-D CUDA tensor, through libmuon.so. The result has
+    G's shape and ``out_dtype`` (bfloat16 like the pages' function)."""
+    if G.dim() != 2:
+        raise ValueError("G must be 2-D")
+    G = G.contiguous()
+    out = torch.empty(G.shape, dtype=out_dtype, device=G.device)
+    plan = MuonPlan([G.shape], [out_dtype], [G.dtype], precision, G.device)
+    plan.newton_schulz([G], [out], make_config(ns_steps=steps))
+    # keep the workspace alive until the stream has passed the call
+    torch.cuda.current_stream().synchronize()
+    plan.close()
+    return out
+
+
+class Muon(torch.optim.Optimizer):
+    """Muon: SGD-Nesterov momentum orthogonalised by Newton-Schulz, for 2-D (or stacked
+    >= 3-D) weight matrices. Each >= 3-D parameter is treated as a stack of matrices over
+    its last two dimensions. 1-D parameters are rejected (they belong to another optimizer).
+    """
+
+    def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, nesterov: bool = True,
+                 ns_steps: int = 5, precision: str = "bf16"):
+        defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, ns_steps=ns_steps)
+        super().__init__(params, defaults)
+        if precision not in _PREC:
+            raise ValueError(f"precision must be one of {sorted(_PREC)}")
+        self.precision = precision
+        for group in self.param_groups:
+            for p in group["params"]:
+                if p.dim() < 2:
+                    raise ValueError("Muon takes matrices only (2-D or stacked >= 3-D params)")
+        self._plans = {}
+
+    @staticmethod
+    def _split(t: torch.Tensor) -> List[torch.Tensor]:
+        if t.dim() == 2:
+            return [t]
+        flat = t.reshape(-1, t.shape[-2], t.shape[-1])
+        return [flat[i] for i in range(flat.shape[0])]
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for gi, group in enumerate(self.param_groups):
+            params, grads, moms = [], [], []
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if not p.is_contiguous() or not p.grad.is_contiguous():
+                    raise ValueError("Muon needs contiguous parameters and gradients")
+                st = self.state[p]
+                if "momentum_buffer" not in st:
+                    st["momentum_buffer"] = torch.zeros(p.shape, dtype=torch.float32,
+                                                        device=p.device)
+                params += self._split(p)
+                grads += self._split(p.grad)
+                moms += self._split(st["momentum_buffer"])
+            if not params:
+                continue
+            key = (gi, tuple((tuple(x.shape), x.dtype, g.dtype) for x, g in zip(params, grads)))
+            plan = self._plans.get(key)
+            if plan is None:
+                plan = MuonPlan([x.shape for x in params], [x.dtype for x in params],
+                                [g.dtype for g in grads], self.precision, params[0].device)
+                self._plans[key] = plan
+            cfg = make_config(lr=group["lr"], beta=group["momentum"],
+                              nesterov=group["nesterov"], ns_steps=group["ns_steps"])
+            plan.step(params, grads, moms, cfg)
+        return loss

@@ -1,0 +1,253 @@
+"""Host-side tests of the C ABI: exported symbols, defaults, plan layout and argument
+validation. Validation errors are raised before any HIP call, so these run without a GPU.
+Calls that pass fake device addresses run only where no GPU is present; the gpu-marked
+variants at the end repeat the checks with real buffers."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from orthogonalized_momentum_optimizer_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake device addresses are only used without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), f"{name} is declared in muon.h but not exported"
+    assert sorted(L.EXPORTED) == names
+
+
+def test_single_hip_runtime_in_process():
+    L.lib()
+    maps = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln]
+    assert len(set(maps)) == 1, set(maps)
+
+
+def test_config_default():
+    c = L.muon_config_default()
+    assert (round(c.lr, 6), round(c.beta, 6), c.nesterov, c.ns_steps) == (0.02, 0.95, 1, 5)
+    assert (round(c.a, 4), round(c.b, 4), round(c.c, 4)) == (3.4445, -4.775, 2.0315)
+    assert abs(c.eps - 1e-7) < 1e-12
+
+
+def test_status_strings():
+    for code, name in [(0, "MUON_OK"), (-1, "MUON_ERR_INVALID_ARG"), (-2, "MUON_ERR_UNSUPPORTED"),
+                       (-3, "MUON_ERR_WORKSPACE"), (-4, "MUON_ERR_HIP")]:
+        assert L.muon_status_string(code) == name
+
+
+def _ws_expected(shapes, esz):
+    """Workspace layout: per padded wide group X0, X1 (count*mp*np), A, B (count*mp*mp),
+    partial sums (count * 64x64 tiles of X), scales (16 B per matrix), each 256-aligned."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    groups = {}
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        key = ((m + 127) // 128 * 128, (n + 127) // 128 * 128)
+        groups[key] = groups.get(key, 0) + 1
+    tot = 0
+    for (mp, np_), cnt in groups.items():
+        tot = al(tot + cnt * mp * np_ * esz)
+        tot = al(tot + cnt * mp * np_ * esz)
+        tot = al(tot + cnt * mp * mp * esz)
+        tot = al(tot + cnt * mp * mp * esz)
+        tot = al(tot + cnt * (mp // 64) * (np_ // 64) * 4)
+        tot = al(tot + cnt * 16)
+    return tot
+
+
+@pytest.mark.parametrize("prec,esz", [(L.MUON_NS_BF16, 2), (L.MUON_NS_F32_DEBUG, 4)])
+def test_plan_workspace_layout(prec, esz):
+    shapes = [(768, 768)] * 4 + [(3072, 768), (768, 3072)] + [(700, 650), (5, 3)]
+    p = L.muon_plan_create([s[0] for s in shapes], [s[1] for s in shapes],
+                           [0] * len(shapes), [0] * len(shapes), prec)
+    try:
+        assert L.muon_plan_workspace_size(p) == _ws_expected(shapes, esz)
+    finally:
+        L.muon_plan_destroy(p)
+
+
+def test_empty_plan():
+    p = L.muon_plan_create([], [], [], [])
+    assert L.muon_plan_workspace_size(p) == 0
+    L.muon_step(p, None, 0, L.muon_config_default(), 0, 0, 0)   # n = 0 is a no-op
+    L.muon_plan_destroy(p)
+
+
+@pytest.mark.parametrize("rows,cols,pdt,gdt,code", [
+    ([0], [4], [0], [0], L.MUON_ERR_INVALID_ARG),
+    ([4], [-1], [0], [0], L.MUON_ERR_INVALID_ARG),
+    ([40000], [4], [0], [0], L.MUON_ERR_UNSUPPORTED),
+    ([20000], [20000], [0], [0], L.MUON_ERR_UNSUPPORTED),
+    ([4], [4], [7], [0], L.MUON_ERR_INVALID_ARG),
+    ([4], [4], [0], [2], L.MUON_ERR_INVALID_ARG),
+])
+def test_plan_create_rejects(rows, cols, pdt, gdt, code):
+    with pytest.raises(L.MuonError) as e:
+        L.muon_plan_create(rows, cols, pdt, gdt)
+    assert e.value.status == code
+    assert L.muon_last_error()
+
+
+def test_plan_create_rejects_bad_precision():
+    with pytest.raises(L.MuonError) as e:
+        L.muon_plan_create([4], [4], [0], [0], 5)
+    assert e.value.status == L.MUON_ERR_INVALID_ARG
+
+
+def test_profile_calls_on_plan():
+    p = L.muon_plan_create([8], [8], [0], [0])
+    prof = L.muon_plan_read_profile(p)
+    assert set(prof) == set(L.KERNEL_KINDS) and all(v == (0.0, 0) for v in prof.values())
+    L.muon_plan_destroy(p)
+
+
+# ---- validation of muon_step / muon_newton_schulz, with fake addresses ---------------------
+
+BASE = 1 << 40   # a fake, 4 KiB aligned device address range; never dereferenced
+
+
+def _fake_call(mutate=None, cfg_mut=None, ws_off=0, ws_bytes=None, n=None):
+    shapes = [(64, 128), (128, 64)]
+    p = L.muon_plan_create([s[0] for s in shapes], [s[1] for s in shapes], [0, 0], [0, 0])
+    ws = L.muon_plan_workspace_size(p)
+    ents = []
+    addr = BASE
+    for r, c in shapes:
+        e = [addr, addr + (1 << 20), addr + (2 << 20), 0, r, c, 0, 0]
+        addr += 4 << 20
+        ents.append(e)
+    if mutate:
+        mutate(ents)
+    mats = L.make_matrices([tuple(e) for e in ents])
+    cfg = L.muon_config_default()
+    if cfg_mut:
+        cfg_mut(cfg)
+    wsp = BASE + (64 << 20) + ws_off
+    try:
+        with pytest.raises(L.MuonError) as e:
+            L.muon_step(p, mats, len(shapes) if n is None else n, cfg, wsp,
+                        ws if ws_bytes is None else ws_bytes, 0)
+        return e.value.status, L.muon_last_error()
+    finally:
+        L.muon_plan_destroy(p)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("case,code", [
+    ("null_param", L.MUON_ERR_INVALID_ARG),
+    ("null_grad", L.MUON_ERR_INVALID_ARG),
+    ("null_momentum", L.MUON_ERR_INVALID_ARG),
+    ("misaligned_grad", L.MUON_ERR_INVALID_ARG),
+    ("misaligned_out", L.MUON_ERR_INVALID_ARG),
+    ("shape_mismatch", L.MUON_ERR_INVALID_ARG),
+    ("dtype_mismatch", L.MUON_ERR_INVALID_ARG),
+    ("param_overlaps_grad", L.MUON_ERR_INVALID_ARG),
+    ("momentum_overlaps_other_param", L.MUON_ERR_INVALID_ARG),
+    ("out_overlaps_grad", L.MUON_ERR_INVALID_ARG),
+])
+def test_step_rejects_matrices(case, code):
+    def mutate(e):
+        if case == "null_param": e[0][0] = 0
+        if case == "null_grad": e[0][1] = 0
+        if case == "null_momentum": e[1][2] = 0
+        if case == "misaligned_grad": e[1][1] += 8
+        if case == "misaligned_out": e[0][3] = BASE + (3 << 20) + 4
+        if case == "shape_mismatch": e[1][4] = 65
+        if case == "dtype_mismatch": e[0][6] = 1
+        if case == "param_overlaps_grad": e[0][1] = e[0][0] + 64
+        if case == "momentum_overlaps_other_param": e[1][2] = e[0][0]
+        if case == "out_overlaps_grad": e[0][3] = e[1][1]
+    status, msg = _fake_call(mutate)
+    assert status == code and msg
+
+
+@no_gpu_only
+def test_step_allows_shared_read_only_gradient():
+    """Two matrices may read the same gradient buffer; the call then passes validation and
+    fails only when it tries to launch (there is no GPU here)."""
+    def mutate(e):
+        e[1][1] = e[0][1]
+        e[1][4], e[1][5] = 128, 64
+    status, msg = _fake_call(mutate)
+    assert status == L.MUON_ERR_HIP, msg
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,value", [("ns_steps", -1), ("ns_steps", 65), ("eps", -1.0),
+                                         ("a", float("nan")), ("lr", float("inf")),
+                                         ("beta", float("nan"))])
+def test_step_rejects_config(field, value):
+    status, _ = _fake_call(cfg_mut=lambda c: setattr(c, field, value))
+    assert status == L.MUON_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_step_rejects_workspace():
+    assert _fake_call(ws_off=16)[0] == L.MUON_ERR_WORKSPACE
+    assert _fake_call(ws_bytes=1024)[0] == L.MUON_ERR_WORKSPACE
+    status, msg = _fake_call(mutate=lambda e: e[0].__setitem__(0, BASE + (64 << 20)))
+    assert status == L.MUON_ERR_INVALID_ARG, msg          # param inside the workspace
+    assert _fake_call(n=1)[0] == L.MUON_ERR_INVALID_ARG   # n differs from the plan
+
+
+@no_gpu_only
+def test_newton_schulz_rejects():
+    p = L.muon_plan_create([64], [96], [0], [0])
+    ws = L.muon_plan_workspace_size(p)
+    cfg = L.muon_config_default()
+    wsp = BASE + (64 << 20)
+    cases = [([0], [BASE]), ([BASE + 8], [BASE + (1 << 20)]), ([BASE], [BASE + 64])]
+    for ins, outs in cases:
+        with pytest.raises(L.MuonError) as e:
+            L.muon_newton_schulz(p, ins, outs, cfg, wsp, ws, 0)
+        assert e.value.status == L.MUON_ERR_INVALID_ARG
+    L.muon_plan_destroy(p)
+
+
+# ---- the same validation with real buffers, on the GPU --------------------------------------
+
+@pytest.mark.gpu
+def test_step_rejects_with_real_buffers():
+    from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config
+    dev = torch.device("cuda", 0)
+    plan = MuonPlan([(64, 128)], [torch.bfloat16], [torch.bfloat16], "bf16", dev)
+    W = torch.zeros(64, 128, dtype=torch.bfloat16, device=dev)
+    G = torch.zeros(64, 128, dtype=torch.bfloat16, device=dev)
+    M = torch.zeros(64, 128, dtype=torch.float32, device=dev)
+    big = torch.zeros(2 * 64 * 128, dtype=torch.float32, device=dev)
+    cfg = make_config()
+    with pytest.raises(L.MuonError) as e:       # momentum 4 bytes off a 16-byte boundary
+        plan.step([W], [G], [big[1:1 + 64 * 128].view(64, 128)], cfg)
+    assert e.value.status == L.MUON_ERR_INVALID_ARG
+    with pytest.raises(L.MuonError) as e:       # update_out overlapping the momentum buffer
+        plan.step([W], [G], [M], cfg, outs=[M])
+    assert e.value.status == L.MUON_ERR_INVALID_ARG
+    with pytest.raises(L.MuonError):
+        cfg.ns_steps = 65
+        plan.step([W], [G], [M], cfg)
+    cfg.ns_steps = 5
+    ws = plan.workspace
+    with pytest.raises(L.MuonError) as e:
+        L.muon_step(plan.handle, plan._matrices([W], [G], [M], None), 1, cfg,
+                    ws.data_ptr(), plan.ws_bytes - 256, torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == L.MUON_ERR_WORKSPACE
+    plan.step([W], [G], [M], cfg)    # valid call still works afterwards
+    torch.cuda.synchronize()
+    plan.close()

@@ -1,0 +1,268 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle, element by
+element, on seeded inputs (run on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from harness import TOL, compare, f64, rel, run_gpu
+from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [(200, 328), (328, 200), (64, 64), (1, 37), (130, 1), (257, 129), (96, 160),
+          (384, 128), (5, 3)]
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_ragged_shapes_full_parity(precision):
+    """Shapes spanning several 128-tiles with ragged tails, wide, tall, vectors and tiny."""
+    _announce(f"ragged shapes {precision}")
+    wl = si.custom(RAGGED, dtype="bf16", steps=3, cfg_id=101)
+    gpu = run_gpu(wl, 3, precision)
+    compare(wl, gpu, 3, precision)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_ragged_shapes_fp32_params(precision):
+    _announce(f"ragged fp32 params {precision}")
+    wl = si.custom([(100, 260), (260, 100), (33, 33)], dtype="f32", steps=2, cfg_id=102,
+                   grad_std=1.0)
+    gpu = run_gpu(wl, 2, precision)
+    compare(wl, gpu, 2, precision)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_gpt2_tiny_fp32_workload(precision):
+    """64x256 fp32 matrix, one N(0,1) gradient reused for 3 steps."""
+    _announce(f"gpt2_tiny_fp32 {precision}")
+    wl = si.WORKLOADS["gpt2_tiny_fp32"]
+    gpu = run_gpu(wl, wl.steps, precision)
+    compare(wl, gpu, wl.steps, precision)
+    # closed form with one reused gradient: W_3 = W_0 - 3 lr NS5(G/||G||)
+    O_ref, _ = oracle.orthogonalize(f64(si.grad(wl, 0, 0)), 5)
+    W3 = gpu[0][-1][0]
+    W0 = f64(si.weight(wl, 0))
+    assert rel(W0 - W3, 3 * 0.02 * O_ref) <= TOL[precision]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_attn_768_workload(precision):
+    _announce(f"attn_768 {precision}")
+    wl = si.WORKLOADS["attn_768"]
+    steps = wl.steps if precision == "bf16" else 3
+    gpu = run_gpu(wl, steps, precision)
+    compare(wl, gpu, steps, precision)
+
+
+def test_gpt2_124m_full_size_sampled():
+    """All 72 matrices of the 124M set in one batched step; a sample of matrices of every
+    shape is compared with the oracle (matrices are independent of each other)."""
+    wl = si.WORKLOADS["gpt2_124m"]
+    watch = si.sample_indices(wl)
+    _announce(f"gpt2_124m full size, watch {watch}")
+    gpu = run_gpu(wl, 3, "bf16", watch=watch)
+    compare(wl, gpu, 3, "bf16")
+
+
+def test_gpt2_124m_full_size_f32_debug_sampled():
+    wl = si.WORKLOADS["gpt2_124m"]
+    watch = [0, 4, 5]
+    _announce(f"gpt2_124m full size f32 debug, watch {watch}")
+    gpu = run_gpu(wl, 2, "f32", watch=watch)
+    compare(wl, gpu, 2, "f32")
+
+
+def test_tall_stress_full_size_sampled():
+    wl = si.WORKLOADS["tall_stress"]
+    watch = si.sample_indices(wl)
+    _announce(f"tall_stress full size, watch {watch}")
+    gpu = run_gpu(wl, 2, "bf16", watch=watch)
+    compare(wl, gpu, 2, "bf16")
+
+
+def test_gpt2_1p5b_full_size_sampled():
+    wl = si.WORKLOADS["gpt2_1p5b"]
+    watch = [0, 4, 287]
+    _announce(f"gpt2_1p5b full size, watch {watch}")
+    gpu = run_gpu(wl, 1, "bf16", watch=watch, gpu_fill_others=True)
+    compare(wl, gpu, 1, "bf16")
+
+
+def test_batch_equals_alone_bitwise():
+    """A matrix's result does not depend on the other matrices of the call."""
+    _announce("batch vs alone")
+    wl = si.custom(RAGGED, dtype="bf16", steps=2, cfg_id=103)
+    batch = run_gpu(wl, 2, "bf16")
+    for i in (0, 1, 5, 7):
+        one = si.custom([RAGGED[i]], dtype="bf16", steps=2, cfg_id=103)
+        grads = [[si.grad(wl, i, t) for t in range(2)]]
+        alone = run_gpu(one, 2, "bf16", grads=grads, W0=[si.weight(wl, i)])
+        for t in range(2):
+            for k in range(3):
+                assert np.array_equal(batch[i][t][k], alone[0][t][k]), (i, t, k)
+
+
+def test_deterministic_bitwise():
+    _announce("determinism")
+    wl = si.custom([(384, 640), (640, 384), (200, 200)], dtype="bf16", steps=2, cfg_id=104)
+    a = run_gpu(wl, 2, "bf16")
+    b = run_gpu(wl, 2, "bf16")
+    for i in a:
+        for t in range(2):
+            for k in range(3):
+                assert np.array_equal(a[i][t][k], b[i][t][k])
+
+
+def test_transpose_path_matches_wide_bitwise():
+    """A tall matrix runs as its transpose: NS(G^T) equals NS(G)^T bit for bit."""
+    _announce("transpose path")
+    dev = torch.device("cuda", 0)
+    G = si.grad(si.custom([(320, 192)], cfg_id=105), 0, 0).to(dev)
+    outs = []
+    for x in (G, G.t().contiguous()):
+        plan = MuonPlan([x.shape], [torch.float32], [x.dtype], "bf16", dev)
+        y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+        plan.newton_schulz([x], [y], make_config())
+        torch.cuda.synchronize()
+        outs.append(f64(y))
+        plan.close()
+    assert np.array_equal(outs[0], outs[1].T)
+
+
+def test_newton_schulz_entry_against_oracle():
+    _announce("newton_schulz entry")
+    dev = torch.device("cuda", 0)
+    wl = si.custom([(256, 512), (512, 256), (100, 100)], cfg_id=106)
+    for prec, odt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        X = [si.grad(wl, i, 0).to(dev) for i in range(wl.n)]
+        Y = [torch.empty(s, dtype=odt, device=dev) for s in wl.shapes]
+        plan = MuonPlan(wl.shapes, [odt] * wl.n, [x.dtype for x in X], prec, dev)
+        plan.newton_schulz(X, Y, make_config(ns_steps=5))
+        torch.cuda.synchronize()
+        plan.close()
+        for i in range(wl.n):
+            ref, _ = oracle.orthogonalize(f64(X[i].cpu()), 5)
+            e = rel(f64(Y[i]), ref)
+            tol = TOL[prec] if odt == torch.float32 else TOL["bf16"]
+            assert e <= tol, (prec, i, e)
+
+
+def test_zero_padding_exact():
+    """A 700x700 matrix and the same matrix zero-padded to 768x768 give identical results
+    on the shared block and exact zeros elsewhere."""
+    _announce("padding")
+    dev = torch.device("cuda", 0)
+    G = si.grad(si.custom([(700, 700)], cfg_id=107), 0, 0).to(dev)
+    P = torch.zeros(768, 768, dtype=G.dtype, device=dev)
+    P[:700, :700] = G
+    ys = []
+    for x in (G, P):
+        plan = MuonPlan([x.shape], [torch.float32], [x.dtype], "bf16", dev)
+        y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+        plan.newton_schulz([x], [y], make_config())
+        torch.cuda.synchronize()
+        plan.close()
+        ys.append(f64(y))
+    assert np.array_equal(ys[1][:700, :700], ys[0])
+    assert not ys[1][700:, :].any() and not ys[1][:, 700:].any()
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_ns_steps_zero_and_one(precision):
+    _announce(f"ns_steps 0/1 {precision}")
+    wl = si.custom([(96, 200), (200, 96)], cfg_id=108, steps=2)
+    for k in (0, 1):
+        gpu = run_gpu(wl, 2, precision, cfg=make_config(ns_steps=k))
+        compare(wl, gpu, 2, precision, oracle_kw=dict(ns_steps=k))
+
+
+def test_non_nesterov_and_other_hyperparameters():
+    _announce("hyper-parameters")
+    wl = si.custom([(128, 384)], cfg_id=109, steps=3)
+    kw = dict(lr=0.05, beta=0.9, nesterov=False)
+    gpu = run_gpu(wl, 3, "bf16", cfg=make_config(**kw))
+    compare(wl, gpu, 3, "bf16", oracle_kw=kw)
+
+
+def test_zero_gradient_leaves_weights():
+    _announce("zero gradient")
+    wl = si.custom([(128, 256), (300, 100)], cfg_id=110, steps=1)
+    grads = [[torch.zeros(s, dtype=torch.bfloat16)] for s in wl.shapes]
+    gpu = run_gpu(wl, 1, "bf16", grads=grads)
+    for i in range(wl.n):
+        W, M, O = gpu[i][0]
+        assert not O.any() and not M.any()
+        assert np.array_equal(W, f64(si.weight(wl, i)))
+
+
+def test_nan_stays_in_its_matrix():
+    _announce("NaN isolation")
+    wl = si.custom([(128, 256), (128, 256), (256, 128)], cfg_id=111, steps=1)
+    clean = [[si.grad(wl, i, 0)] for i in range(wl.n)]
+    dirty = [[g[0].clone()] for g in clean]
+    dirty[1][0][5, 7] = float("nan")
+    a = run_gpu(wl, 1, "bf16", grads=clean)
+    b = run_gpu(wl, 1, "bf16", grads=dirty)
+    assert np.isnan(b[1][0][2]).any()
+    for i in (0, 2):
+        for k in range(3):
+            assert np.array_equal(a[i][0][k], b[i][0][k])
+
+
+def test_resume_bitwise():
+    """4 steps equal 2 steps, a copy of (W, M) into fresh buffers, and 2 more steps."""
+    _announce("resume")
+    dev = torch.device("cuda", 0)
+    wl = si.custom([(192, 320), (320, 192)], cfg_id=112, steps=4)
+    cfg = make_config()
+
+    def fresh():
+        W = [si.weight(wl, i).to(dev) for i in range(wl.n)]
+        M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in wl.shapes]
+        return W, M
+
+    plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16", dev)
+    W, M = fresh()
+    for t in range(4):
+        plan.step(W, [si.grad(wl, i, t).to(dev) for i in range(wl.n)], M, cfg)
+    W2, M2 = fresh()
+    for t in range(2):
+        plan.step(W2, [si.grad(wl, i, t).to(dev) for i in range(wl.n)], M2, cfg)
+    torch.cuda.synchronize()
+    W3 = [w.cpu().to(dev) for w in W2]
+    M3 = [m.cpu().to(dev) for m in M2]
+    for t in range(2, 4):
+        plan.step(W3, [si.grad(wl, i, t).to(dev) for i in range(wl.n)], M3, cfg)
+    torch.cuda.synchronize()
+    plan.close()
+    for i in range(wl.n):
+        assert torch.equal(W[i], W3[i]) and torch.equal(M[i], M3[i])
+
+
+def test_output_band_of_quintic():
+    """Singular values of the GPU result follow p^5 of the normalised input singular values
+    within bf16 error, and stay inside the band of the 5-fold map."""
+    _announce("band")
+    dev = torch.device("cuda", 0)
+    for k, shp in enumerate([(64, 256), (256, 768)]):
+        x = si.grad(si.custom([shp], cfg_id=113 + k), 0, 0).to(dev)
+        plan = MuonPlan([shp], [torch.float32], [x.dtype], "bf16", dev)
+        y = torch.empty(shp, dtype=torch.float32, device=dev)
+        plan.newton_schulz([x], [y], make_config())
+        torch.cuda.synchronize()
+        plan.close()
+        xs = f64(x)
+        s_in = np.sort(np.linalg.svd(xs, compute_uv=False) / np.linalg.norm(xs))
+        s_out = np.sort(np.linalg.svd(f64(y), compute_uv=False))
+        a, b, c = oracle.DEFAULT_ABC
+        s5 = s_in.copy()
+        for _ in range(5):
+            s5 = a * s5 + b * s5 ** 3 + c * s5 ** 5
+        assert np.max(np.abs(np.sort(s5) - s_out)) < 0.05
+        assert s_out.max() < 1.202369 + 0.05 and s_out.min() > 0.681831 - 0.05
