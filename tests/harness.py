@@ -10,6 +10,9 @@ import seeded_inputs as si
 from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config
 
 TOL = {"bf16": 3e-2, "f32": 1e-4}        # relative Frobenius error of O and W
+# A weight stored in bf16 carries a relative rounding of up to 2^-9 per element after
+# every update, whatever the precision of the Newton-Schulz rounds; such weights are
+# compared at the bf16 tolerance, weights stored in fp32 at the tolerance of the rounds.
 M_TOL = 1e-6                             # momentum: max |dM| / max |M| (fp32 buffer)
 
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -77,6 +80,7 @@ def compare(wl, gpu, steps, precision, grads=None, report=None, oracle_kw=None):
     """Element-by-element comparison of every watched matrix and step with the oracle.
     Returns the worst (O error, W error, M error)."""
     tol = TOL[precision]
+    w_tol = max(tol, TOL["bf16"]) if wl.dtype == "bf16" else tol
     worst = [0.0, 0.0, 0.0]
     for i, traj in gpu.items():
         ref = run_oracle(wl, i, steps, grads=grads, **(oracle_kw or {}))
@@ -88,7 +92,7 @@ def compare(wl, gpu, steps, precision, grads=None, report=None, oracle_kw=None):
             if report is not None:
                 report.append((i, t, eo, ew, em))
             assert eo <= tol, f"matrix {i} {wl.shapes[i]} step {t}: O rel err {eo:.3e} > {tol}"
-            assert ew <= tol, f"matrix {i} step {t}: W rel err {ew:.3e} > {tol}"
+            assert ew <= w_tol, f"matrix {i} step {t}: W rel err {ew:.3e} > {w_tol}"
             assert em <= M_TOL, f"matrix {i} step {t}: M rel err {em:.3e} > {M_TOL}"
     print(f"{wl.name} [{precision}] worst O {worst[0]:.3e}  W {worst[1]:.3e}  M {worst[2]:.3e}",
           flush=True)
