@@ -33,6 +33,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kChunks = BK / 8;  // 16-byte chunks per LDS row
@@ -66,6 +69,37 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// fp32 staging tile of the epilogue: 128 rows of 32 chunks of 4 floats, chunk XOR row swizzle.
+__device__ __forceinline__ int stage_idx(int row, int col) {
+  return row * 128 + ((((col >> 2) ^ swz(row)) << 2) | (col & 3));
+}
+
+// Epilogue arithmetic on 8 consecutive outputs, one 16-byte store (and one 16-byte load of
+// the epilogue operand): GRAM v = s*acc, POLY v = alpha*A + beta*acc, APPLY v = s*(alpha*X + acc).
+template <int MODE>
+__device__ __forceinline__ void store_chunk(uint16_t* dst, const uint16_t* epi, const float a[8],
+                                            float s, float alpha, float beta) {
+  u32x4 e4 = {0u, 0u, 0u, 0u};
+  if (MODE != 0) e4 = *reinterpret_cast<const u32x4*>(epi);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v0, v1;
+    if (MODE == 0) {
+      v0 = a[2 * q] * s;
+      v1 = a[2 * q + 1] * s;
+    } else if (MODE == 1) {
+      v0 = fmaf(alpha, bf2f(e4[q] & 0xffffu), beta * a[2 * q]);
+      v1 = fmaf(alpha, bf2f(e4[q] >> 16), beta * a[2 * q + 1]);
+    } else {
+      v0 = fmaf(alpha, bf2f(e4[q] & 0xffffu), a[2 * q]) * s;
+      v1 = fmaf(alpha, bf2f(e4[q] >> 16), a[2 * q + 1]) * s;
+    }
+    o[q] = f2bf(v0) | (f2bf(v1) << 16);
+  }
+  *reinterpret_cast<u32x4*>(dst) = o;
+}
+
 // Block id -> logical tile so that each XCD (id % 8) receives a contiguous logical range.
 __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int q = total >> 3, r = total & 7;
@@ -74,17 +108,17 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 }
 
 // Stage a 128 x 64 K-contiguous tile: thread t moves chunk (t & 7) of rows (t >> 3) + 32 i.
-__device__ __forceinline__ void load_kmajor(const uint16_t* src, int ld, uint4 reg[4]) {
+__device__ __forceinline__ void load_kmajor(const uint16_t* src, int ld, u32x4 reg[4]) {
   const int t = threadIdx.x;
   const int c = t & 7;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (t >> 3) + 32 * i;
-    reg[i] = *reinterpret_cast<const uint4*>(src + (size_t)r * ld + 8 * c);
+    reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + 8 * c);
   }
 }
 
-__device__ __forceinline__ void store_kmajor(uint4* lds, const uint4 reg[4]) {
+__device__ __forceinline__ void store_kmajor(u32x4* lds, const u32x4 reg[4]) {
   const int t = threadIdx.x;
   const int c = t & 7;
 #pragma unroll
@@ -96,29 +130,29 @@ __device__ __forceinline__ void store_kmajor(uint4* lds, const uint4 reg[4]) {
 
 // Stage a 64(k) x 128(n) N-contiguous tile as 128 rows of 64 K-values: thread t loads rows
 // 4p..4p+3 (p = t >> 4) at columns 8q..8q+7 (q = t & 15).
-__device__ __forceinline__ void load_nmajor(const uint16_t* src, int ld, uint4 reg[4]) {
+__device__ __forceinline__ void load_nmajor(const uint16_t* src, int ld, u32x4 reg[4]) {
   const int t = threadIdx.x;
   const int p = t >> 4, q = t & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    reg[i] = *reinterpret_cast<const uint4*>(src + (size_t)(4 * p + i) * ld + 8 * q);
+    reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(4 * p + i) * ld + 8 * q);
 }
 
-__device__ __forceinline__ uint32_t half_of(const uint4& v, int d, int h) {
-  const uint32_t w = d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int d, int h) {
+  const uint32_t w = v[d];
   return h ? (w >> 16) : (w & 0xffffu);
 }
 
-__device__ __forceinline__ void store_nmajor(uint4* lds, const uint4 reg[4]) {
+__device__ __forceinline__ void store_nmajor(u32x4* lds, const u32x4 reg[4]) {
   const int t = threadIdx.x;
   const int p = t >> 4, q = t & 15;
-  uint2* l2 = reinterpret_cast<uint2*>(lds);
+  u32x2* l2 = reinterpret_cast<u32x2*>(lds);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n = 8 * q + 2 * d + h;  // LDS row
-      uint2 v;
+      u32x2 v;
       v.x = half_of(reg[0], d, h) | (half_of(reg[1], d, h) << 16);
       v.y = half_of(reg[2], d, h) | (half_of(reg[3], d, h) << 16);
       const int chunk = (p >> 1) ^ swz(n);
@@ -129,8 +163,9 @@ __device__ __forceinline__ void store_nmajor(uint4* lds, const uint4 reg[4]) {
 
 template <int MODE>
 __global__ __launch_bounds__(256) void ns_gemm_bf16(GemmArgs g) {
-  __shared__ uint4 sA[2][BM * kChunks];
-  __shared__ uint4 sB[2][BN * kChunks];
+  // operand tiles: A stages at [0, 2048), B stages at [2048, 4096) (16-byte units)
+  __shared__ u32x4 smem[4 * BM * kChunks];
+  constexpr int kStage = BM * kChunks;
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -161,15 +196,15 @@ __global__ __launch_bounds__(256) void ns_gemm_bf16(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[4], rb[4];
+  u32x4 ra[4], rb[4];
   const int KT = g.K / BK;
 
   load_kmajor(lhs, g.ld_lhs, ra);
   if (MODE == APPLY) load_nmajor(rhs, g.ld_rhs, rb);
   else load_kmajor(rhs, g.ld_rhs, rb);
-  store_kmajor(sA[0], ra);
-  if (MODE == APPLY) store_nmajor(sB[0], rb);
-  else store_kmajor(sB[0], rb);
+  store_kmajor(smem, ra);
+  if (MODE == APPLY) store_nmajor(smem + 2 * kStage, rb);
+  else store_kmajor(smem + 2 * kStage, rb);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
@@ -181,8 +216,8 @@ __global__ __launch_bounds__(256) void ns_gemm_bf16(GemmArgs g) {
       if (MODE == APPLY) load_nmajor(rhs + (size_t)k0 * g.ld_rhs, g.ld_rhs, rb);
       else load_kmajor(rhs + k0, g.ld_rhs, rb);
     }
-    const uint4* A = sA[cur];
-    const uint4* B = sB[cur];
+    const u32x4* A = smem + cur * kStage;
+    const u32x4* B = smem + (2 + cur) * kStage;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int c = 2 * ks + (lane >> 5);
@@ -190,13 +225,13 @@ __global__ __launch_bounds__(256) void ns_gemm_bf16(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wr * 64 + i * 32 + (lane & 31);
-        const uint4 v = A[row * kChunks + (c ^ swz(row))];
+        const u32x4 v = A[row * kChunks + (c ^ swz(row))];
         af[i] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = wc * 64 + j * 32 + (lane & 31);
-        const uint4 v = B[row * kChunks + (c ^ swz(row))];
+        const u32x4 v = B[row * kChunks + (c ^ swz(row))];
         bfr[j] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
@@ -206,65 +241,70 @@ __global__ __launch_bounds__(256) void ns_gemm_bf16(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (more) {
-      store_kmajor(sA[cur ^ 1], ra);
-      if (MODE == APPLY) store_nmajor(sB[cur ^ 1], rb);
-      else store_kmajor(sB[cur ^ 1], rb);
+      store_kmajor(smem + (cur ^ 1) * kStage, ra);
+      if (MODE == APPLY) store_nmajor(smem + (2 + (cur ^ 1)) * kStage, rb);
+      else store_kmajor(smem + (2 + (cur ^ 1)) * kStage, rb);
     }
     __syncthreads();
   }
 
-  // Epilogue. Accumulator element r of lane l in a 32x32 block sits at
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // Epilogue, staged through LDS so that every global access is a 16-byte row segment.
+  // The fp32 tile (128 x 128, 64 KB) reuses the operand buffers; its 16-byte chunks are
+  // XOR-swizzled by the row like the operand tiles. Accumulator element r of lane l in a
+  // 32x32 block sits at row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wc * 64 + j * 32 + (lane & 31);
+        st[stage_idx(row, col)] = acc[i][j][r];
+      }
+  __syncthreads();
+
   float s = 1.f;
   if (g.scales) s = g.scales[4 * bidx + g.scale_idx];
   uint16_t* out = g.out + bidx * g.out_bs;
   const uint16_t* epi = (MODE == GRAM) ? nullptr : g.epi + bidx * g.out_bs;
   const int ld = g.ld_out;
   const bool diag = (MODE != APPLY) && (I == J);
-  const bool mirror = (MODE != APPLY) && (I != J);
 
+  // Row pass: output tile (I, J). Thread t takes 8-column chunks (t % 16) of rows t / 16 + 16k.
+  // On a diagonal tile the lower triangle takes the upper triangle's values, so the stored
+  // matrix is exactly symmetric.
+#pragma unroll 2
+  for (int k = 0; k < 8; ++k) {
+    const int row = (t >> 4) + 16 * k, ch = t & 15;
+    float a[8];
+    if (diag) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gj = J * BN + wc * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int gi0 = I * BM + wr * 64 + i * 32 + 8 * rg + 4 * (lane >> 5);
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gi = gi0 + r;
-          const float a = acc[i][j][4 * rg + r];
-          if (MODE == GRAM) {
-            v[r] = a * s;
-          } else if (MODE == POLY) {
-            v[r] = fmaf(g.alpha, bf2f(epi[(size_t)gi * ld + gj]), g.beta * a);
-          } else {
-            v[r] = (fmaf(g.alpha, bf2f(epi[(size_t)gi * ld + gj]), a)) * s;
-          }
-        }
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f2bf(v[r]);
-        if (diag) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int gi = gi0 + r;
-            if (gi <= gj) out[(size_t)gi * ld + gj] = (uint16_t)h[r];
-            if (gi < gj) out[(size_t)gj * ld + gi] = (uint16_t)h[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) out[(size_t)(gi0 + r) * ld + gj] = (uint16_t)h[r];
-          if (mirror) {
-            uint2 w;
-            w.x = h[0] | (h[1] << 16);
-            w.y = h[2] | (h[3] << 16);
-            *reinterpret_cast<uint2*>(out + (size_t)gj * ld + gi0) = w;
-          }
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int col = 8 * ch + e;
+        a[e] = col >= row ? st[stage_idx(row, col)] : st[stage_idx(col, row)];
       }
+    } else {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(st + stage_idx(row, 8 * ch));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(st + stage_idx(row, 8 * ch + 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+    }
+    const size_t off = (size_t)(I * BM + row) * ld + J * BN + 8 * ch;
+    store_chunk<MODE>(out + off, MODE == GRAM ? nullptr : epi + off, a, s, g.alpha, g.beta);
+  }
+
+  // Mirror pass: for an off-diagonal symmetric tile, tile (J, I) is the transpose.
+  if (MODE != APPLY && I != J) {
+#pragma unroll 2
+    for (int k = 0; k < 8; ++k) {
+      const int col = (t >> 4) + 16 * k, ch = t & 15;   // output row = col, columns = rows
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = st[stage_idx(8 * ch + e, col)];
+      const size_t off = (size_t)(J * BN + col) * ld + I * BM + 8 * ch;
+      store_chunk<MODE>(out + off, MODE == GRAM ? nullptr : epi + off, a, s, g.alpha, g.beta);
     }
   }
 }
