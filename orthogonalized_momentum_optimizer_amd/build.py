@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_gemm_f32.hip"]
+SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -69,7 +69,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(one, SOURCES))
     tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

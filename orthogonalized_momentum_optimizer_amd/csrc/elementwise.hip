@@ -18,12 +18,14 @@ namespace {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays NaN (quiet bit set).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 in one dword (lo = first), round to nearest even, NaN stays
+// NaN: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int DT>
@@ -48,7 +50,7 @@ __device__ __forceinline__ void load4(const void* p, size_t i, float v[4]) {
 
 template <int DT>
 __device__ __forceinline__ void store1(void* p, size_t i, float v) {
-  if (DT == 0) static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
+  if (DT == 0) static_cast<uint16_t*>(p)[i] = (uint16_t)(pack_bf16(v, 0.f) & 0xffffu);
   else static_cast<float*>(p)[i] = v;
 }
 
@@ -56,8 +58,8 @@ template <int DT>
 __device__ __forceinline__ void store4(void* p, size_t i, const float v[4]) {
   if (DT == 0) {
     uint2 w;
-    w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    w.x = pack_bf16(v[0], v[1]);
+    w.y = pack_bf16(v[2], v[3]);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);

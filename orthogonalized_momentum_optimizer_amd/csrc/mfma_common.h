@@ -1,0 +1,142 @@
+// Device helpers shared by the bf16 Newton-Schulz product kernels (gfx950).
+//
+// Operand tiles move global -> LDS with 16-byte direct-to-LDS loads (global_load_lds):
+// a wave instruction fills 1 KB of LDS linearly (lane l at byte 16 l), so the XOR swizzles
+// below are applied by choosing which global 16-byte chunk each lane fetches.
+//
+//  - K-contiguous tiles: ROWS rows x 32 K-values (4 chunks of 16 bytes per row); chunk c of
+//    row r is stored at c ^ ((r >> 2) & 3). A fragment read (16 consecutive lanes = 16
+//    consecutive rows, same chunk) then covers all 64 LDS banks (measured conflict-free;
+//    keying on bits 1-2 of the row measured 2-way conflicted).
+//  - N-contiguous tiles: 32 K-rows x COLS N-values (COLS/8 chunks per row); chunk c of K-row
+//    k is stored at c ^ 2(k & 3). Fragments come from ds_read_b64_tr_b16: in each 16-lane
+//    group, lanes 4e..4e+3 point at the 4 consecutive N-values of K-row e they cover, and lane
+//    i receives the 4 K-values of column i; the 4 rows x 32 bytes of a group then fall on 8
+//    distinct 16-byte bank groups.
+#pragma once
+
+#include "muon_internal.h"
+
+namespace muon {
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+#define MUON_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 in one dword (lo = first), round to nearest even, NaN stays
+// NaN: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Block id -> logical tile. Block ids are dealt to the 8 XCDs round robin (id % 8); the
+// remap gives each XCD a contiguous logical range, so consecutive tiles of one matrix share
+// an XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = w & 7, s = w >> 3;
+  return (x < r) ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+// vmcnt <= N for this wave's outstanding vector-memory loads (lgkm and exp unconstrained).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+
+// K-contiguous ROWS x 32 tile (rows row0.. of `src`, K from k0) into `stage` (16-byte units at
+// row*4 + chunk). Rows at or beyond `row_end` are fetched from row_end - 1 instead (their
+// products are never stored). With NW waves each wave issues ROWS/(16 NW) 1 KB blocks.
+template <int ROWS, int NW>
+__device__ __forceinline__ void dma_kmajor(const uint16_t* src, int ld, int row0, int row_end,
+                                           int k0, u32x4* stage) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kPerWave = ROWS / 16 / NW;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int blk = kPerWave * w + i;
+    const int row = 16 * blk + (lane >> 2);
+    const int c = (lane & 3) ^ kswz(row);
+    const int grow = min(row0 + row, row_end - 1);
+    __builtin_amdgcn_global_load_lds(src + (size_t)grow * ld + k0 + 8 * c,
+                                     MUON_LDS_PTR(stage + 64 * blk), 16, 0, 0);
+  }
+}
+
+// N-contiguous 32(k) x COLS(n) tile (K-rows k0.. of `src`, columns col0..) into `stage`
+// (units at k*(COLS/8) + chunk). Columns at or beyond `col_end` (a multiple of 8) are fetched
+// from the last valid chunk instead.
+template <int COLS, int NW>
+__device__ __forceinline__ void dma_nmajor(const uint16_t* src, int ld, int k0, int col0,
+                                           int col_end, u32x4* stage) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kChunks = COLS / 8, kRowsPerBlk = 64 / kChunks;
+  constexpr int kPerWave = 32 / kRowsPerBlk / NW;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int blk = kPerWave * w + i;
+    const int k = kRowsPerBlk * blk + lane / kChunks;
+    const int c = (lane % kChunks) ^ (2 * (k & 3));
+    const int gcol = min(col0 + 8 * c, col_end - 8);
+    __builtin_amdgcn_global_load_lds(src + (size_t)(k0 + k) * ld + gcol,
+                                     MUON_LDS_PTR(stage + 64 * blk), 16, 0, 0);
+  }
+}
+
+// One K-contiguous fragment: 8 K-values (chunk c) of LDS row `row`.
+__device__ __forceinline__ bf16x8 frag_k(const u32x4* stage, int row, int c) {
+  return __builtin_bit_cast(bf16x8, stage[row * 4 + (c ^ kswz(row))]);
+}
+
+// ds_read_b64_tr_b16 issued as inline assembly: through the builtin, the compiler waits for
+// every outstanding direct-to-LDS load (vmcnt 0) before the read, which would drain the load
+// pipeline each step. The result is valid only after lds_wait().
+__device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
+  const unsigned addr = static_cast<unsigned>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// Waits for this wave's LDS reads; ties the fragments to the wait so no use moves above it.
+__device__ __forceinline__ void lds_wait(bf16x8& x, bf16x8& y) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y));
+}
+
+// One transposed fragment of an N-contiguous tile with COLS columns: lane l gets K-values
+// kb + 8(l/32) + 0..7 of column nb + l%32 (valid after lds_wait).
+template <int COLS>
+__device__ __forceinline__ bf16x8 frag_n(const u32x4* stage, int kb, int nb, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int n = nb + 16 * (g & 1) + 4 * (j & 3);
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(stage);
+  s16x4 h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = kb + 8 * (g >> 1) + 4 * half + (j >> 2);
+    const int c = (n >> 3) ^ (2 * (k & 3));
+    h[half] = ds_read_tr(base + k * COLS + 8 * c + (n & 7));
+  }
+  const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace mfma
+}  // namespace muon

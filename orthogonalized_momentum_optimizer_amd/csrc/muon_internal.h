@@ -51,11 +51,14 @@ struct NsGroup {
   int batch, mp, np;
   int first;           // first round: fold the 1/nu normalisation into the epilogues
 };
-// bf16 storage, bf16 matrix cores with fp32 accumulation (ns_gemm_bf16.hip)
-hipError_t launch_gram_bf16(const NsGroup& g, hipStream_t s);                    // A = s2 X X^T
-hipError_t launch_poly_bf16(const NsGroup& g, float b, float c, hipStream_t s);  // B = bA + cAA
-hipError_t launch_apply_bf16(const NsGroup& g, float a, hipStream_t s);          // X' = s1(aX+BX)
-// fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip)
+// bf16 storage, bf16 matrix cores with fp32 accumulation (ns_gemm_bf16.hip, ns_apply_bf16.hip).
+// The bf16 round folds a I into B: poly writes B' = aI + bA + cAA and apply forms s1 B' X.
+hipError_t launch_gram_bf16(const NsGroup& g, hipStream_t s);   // A = s2 X X^T
+hipError_t launch_poly_bf16(const NsGroup& g, float a, float b, float c,
+                            hipStream_t s);                     // B' = aI + bA + cAA
+hipError_t launch_apply_bf16(const NsGroup& g, hipStream_t s);  // X' = s1 B' X
+// fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip): B = bA + cAA and
+// X' = s1 (aX + BX), the round as written
 hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);
 hipError_t launch_poly_f32(const NsGroup& g, float b, float c, hipStream_t s);
 hipError_t launch_apply_f32(const NsGroup& g, float a, hipStream_t s);

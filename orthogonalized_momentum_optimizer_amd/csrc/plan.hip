@@ -231,10 +231,10 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
             [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(N, stream); });
       L.run(MUON_KERNEL_POLY, "poly", [&] {
         return f32 ? launch_poly_f32(N, cfg->b, cfg->c, stream)
-                   : launch_poly_bf16(N, cfg->b, cfg->c, stream);
+                   : launch_poly_bf16(N, cfg->a, cfg->b, cfg->c, stream);
       });
       L.run(MUON_KERNEL_APPLY, "apply", [&] {
-        return f32 ? launch_apply_f32(N, cfg->a, stream) : launch_apply_bf16(N, cfg->a, stream);
+        return f32 ? launch_apply_f32(N, cfg->a, stream) : launch_apply_bf16(N, stream);
       });
       std::swap(xin, xout);
     }
