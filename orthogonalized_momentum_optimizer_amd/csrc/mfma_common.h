@@ -115,6 +115,16 @@ __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
   return r;
 }
 
+// 16-byte LDS read issued as inline assembly (see ds_read_tr): valid only after an explicit
+// lgkmcnt wait that names the result.
+__device__ __forceinline__ u32x4 ds_read_b128(const u32x4* p) {
+  const unsigned addr = static_cast<unsigned>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
 // Waits for this wave's LDS reads; ties the fragments to the wait so no use moves above it.
 __device__ __forceinline__ void lds_wait(bf16x8& x, bf16x8& y) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y));

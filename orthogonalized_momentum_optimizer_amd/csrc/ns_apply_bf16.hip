@@ -68,36 +68,72 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = g.mp / TK;
-  auto issue = [&](int kt) {
+
+  // ---- memory operations, one instruction each, so they can be interleaved with MFMAs ----
+  // Direct-to-LDS loads of stage kt: ops 0-3 fetch left-operand rows, 4-7 right-operand rows.
+  auto dma_op = [&](int kt, int op) {
     u32x4* st = smem + (kt % NSTAGE) * kUnitsStage;
-    dma_kmajor<TM, 4>(lhs, g.mp, row0, g.mp, kt * TK, st);
-    dma_nmajor<TN, 4>(rhs, g.np, kt * TK, col0, g.np, st + kUnitsA);
+    if (op < 4) {
+      const int blk = 4 * wave + op;
+      const int row = 16 * blk + (lane >> 2);
+      const int c = (lane & 3) ^ kswz(row);
+      const int grow = min(row0 + row, g.mp - 1);
+      __builtin_amdgcn_global_load_lds(lhs + (size_t)grow * g.mp + kt * TK + 8 * c,
+                                       MUON_LDS_PTR(st + 64 * blk), 16, 0, 0);
+    } else {
+      const int blk = 4 * wave + (op - 4);
+      const int k = 2 * blk + (lane >> 5);
+      const int c = (lane & 31) ^ (2 * (k & 3));
+      const int gcol = min(col0 + 8 * c, g.np - 8);
+      __builtin_amdgcn_global_load_lds(rhs + (size_t)(kt * TK + k) * g.np + gcol,
+                                       MUON_LDS_PTR(st + kUnitsA + 64 * blk), 16, 0, 0);
+    }
   };
-  // Fragments of one 16-wide K slice (ks = 0, 1) of a stage.
-  auto load = [&](int kt, int ks, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+  // LDS reads of one 16-wide K slice (ks) of stage kt: ops 0-7 are the transposing reads of
+  // the right-operand fragments (fragment op/2, half op%2), ops 8-11 the left fragments.
+  struct Frags {
+    s16x4 bh[4][2];
+    u32x4 av[4];
+  };
+  auto lds_op = [&](int kt, int ks, int op, Frags& f) {
     const u32x4* A = smem + (kt % NSTAGE) * kUnitsStage;
-    const u32x4* B = A + kUnitsA;
-    const int c = 2 * ks + (lane >> 5);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = frag_n<TN>(B, 16 * ks, wc * 128 + j * 32, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = frag_k(A, wr * 128 + i * 32 + (lane & 31), c);
+    if (op < 8) {
+      const int j = op >> 1, half = op & 1;
+      const int grp = lane >> 4, jj = lane & 15;
+      const int n = wc * 128 + j * 32 + 16 * (grp & 1) + 4 * (jj & 3);
+      const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (jj >> 2);
+      const int c = (n >> 3) ^ (2 * (k & 3));
+      f.bh[j][half] = ds_read_tr(reinterpret_cast<const uint16_t*>(A + kUnitsA) + k * TN + 8 * c +
+                                 (n & 7));
+    } else {
+      const int i = op - 8;
+      const int row = wr * 128 + i * 32 + (lane & 31);
+      const int c = 2 * ks + (lane >> 5);
+      f.av[i] = ds_read_b128(A + row * 4 + (c ^ kswz(row)));
+    }
   };
-  auto wait_frags = [&](bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
-    lds_wait(bf[0], bf[1]);
-    lds_wait(bf[2], bf[3]);
-    lds_wait(af[0], af[1]);
-    lds_wait(af[2], af[3]);
-  };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+  // Waits for the reads of `f` (and every earlier LDS read of this wave), then assembles the
+  // MFMA operands; the assembly depends on the wait, so it cannot move above it.
+  auto ready = [&](Frags& f, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.bh[0][0]), "+v"(f.bh[0][1]), "+v"(f.bh[1][0]), "+v"(f.bh[1][1]),
+                   "+v"(f.bh[2][0]), "+v"(f.bh[2][1]), "+v"(f.bh[3][0]), "+v"(f.bh[3][1]),
+                   "+v"(f.av[0]), "+v"(f.av[1]), "+v"(f.av[2]), "+v"(f.av[3]));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const s16x8 v = {f.bh[j][0][0], f.bh[j][0][1], f.bh[j][0][2], f.bh[j][0][3],
+                       f.bh[j][1][0], f.bh[j][1][1], f.bh[j][1][2], f.bh[j][1][3]};
+      bf[j] = __builtin_bit_cast(bf16x8, v);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, f.av[i]);
   };
-  // Waits for this wave's loads of stage `next`, given how many later stages were issued,
-  // then the block barrier: stage `next` is complete for every wave.
+  auto mfma = [&](int m, const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+    const int i = m >> 2, j = m & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  // Waits for this wave's loads of the next stage (`later` stages issued after it), then the
+  // block barrier: that stage is complete for every wave.
   auto stage_ready = [&](int later) {
     if (later >= 3) vm_wait<3 * kLoadsPerStage>();
     else if (later == 2) vm_wait<2 * kLoadsPerStage>();
@@ -107,33 +143,48 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
   };
 
-  // Software pipeline: each stage's two K slices are read into registers one slice ahead of
-  // the 16 MFMAs that use them, and the barrier for the next stage is taken right after a
-  // batch of MFMAs is issued, so LDS reads, direct loads and the barrier all run in the
-  // shadow of the matrix cores. Stages are prefetched four ahead (all four buffers in use).
+  // ---- software pipeline ----
+  // Per stage, two batches of 16 MFMAs (one per K slice). While batch 0 runs, the 12 reads
+  // of slice 1 are issued between its MFMAs; then (slice 1 in registers, so this wave is done
+  // with the stage) the next stage's barrier; while batch 1 runs, the 8 direct loads of stage
+  // kt + 4 (into this stage's buffer) and the 12 reads of the next stage's slice 0 are issued
+  // between its MFMAs. sched_barrier fences pin that order.
 #pragma unroll
   for (int s = 0; s < NSTAGE; ++s)
-    if (s < KT) issue(s);
+    if (s < KT)
+      for (int op = 0; op < 8; ++op) dma_op(s, op);
   stage_ready(min(NSTAGE - 1, KT - 1));
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  load(0, 0, a0, b0);
-  wait_frags(a0, b0);
+  Frags f0, f1;
+#pragma unroll
+  for (int op = 0; op < 12; ++op) lds_op(0, 0, op, f0);
+  ready(f0, a0, b0);
 
   for (int kt = 0; kt < KT; ++kt) {
-    load(kt, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_frags(a1, b1);  // slice 1 is in registers: this wave is done reading stage kt
-    if (kt + 1 < KT) {
-      stage_ready(min(NSTAGE - 2, KT - 2 - kt));
-      if (kt + NSTAGE < KT) issue(kt + NSTAGE);  // into stage kt's buffer, now free
-      load(kt + 1, 0, a0, b0);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma(m, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < 12) lds_op(kt, 1, m, f1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    ready(f1, a1, b1);  // slice 1 is in registers: this wave is done reading stage kt
+    const bool more = kt + 1 < KT;
+    if (more) stage_ready(min(NSTAGE - 2, KT - 2 - kt));
+    const bool refill = kt + NSTAGE < KT;
     __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) wait_frags(a0, b0);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma(m, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < 8) {
+        if (refill) dma_op(kt + NSTAGE, m);
+      }
+      if (more && m >= 2 && m < 14) lds_op(kt + 1, 0, m - 2, f0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) ready(f0, a0, b0);
   }
 
   // Epilogue: scale, round to bf16 and stage the 256x256 tile in LDS (128 KB, the whole
