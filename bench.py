@@ -51,6 +51,33 @@ def kind_work(wl, ns_steps=5):
     return w
 
 
+KERNEL_SOURCES = {   # kernel kind -> the source file that defines its bf16 kernel
+    "apply": "ns_apply_bf16.hip", "gram": "ns_gemm_bf16.hip", "poly": "ns_gemm_bf16.hip",
+    "momentum": "elementwise.hip", "update": "elementwise.hip", "norm": "elementwise.hip",
+}
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per launch of a kernel kind, from the rocprofv3 counter summary committed
+    under profiles/ (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy of known
+    size). None when there is no summary or the kernel's source changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.md")
+    src = os.path.join(ROOT, "orthogonalized_momentum_optimizer_amd", "csrc",
+                       KERNEL_SOURCES.get(kind, ""))
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m_b or not m_h:
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
+        return None
+    return float(m_b.group(1))
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle, as it stands, on whole matrices of the workload (one step from zero
     momentum each), in workload order until ``budget_s`` is spent; scaled to one full step
@@ -95,6 +122,9 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before timing, copy 256 MiB device to device once (a plain copy of "
+                         "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +146,14 @@ def main():
     stream = torch.cuda.current_stream()
     print(f"[bench] workspace {plan.ws_bytes / 2**20:.1f} MiB; warmup {args.warmup}",
           file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for t in range(args.warmup):
         plan.step(W, G[t % 2], M, cfg)
@@ -171,14 +209,16 @@ def main():
         if dom in ("gram", "poly", "apply"):
             ach = work[dom] * args.steps / (dms * 1e-3) / 1e12
             out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak_mm,
-                               "unit": "TFLOP/s", "frac": ach / peak_mm, "traffic": None,
+                               "unit": "TFLOP/s", "frac": ach / peak_mm,
+                               "traffic": measured_traffic(dom, wl.name),
                                "avg_launch_us": 1e3 * dms / max(dl, 1),
                                "work_per_launch": work[dom] * args.steps / max(dl, 1)}
         else:
             ach = work.get(dom, 0.0) * args.steps / (dms * 1e-3) / 1e9
             out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach,
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                               "traffic": None, "avg_launch_us": 1e3 * dms / max(dl, 1)}
+                               "traffic": measured_traffic(dom, wl.name),
+                               "avg_launch_us": 1e3 * dms / max(dl, 1)}
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
