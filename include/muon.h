@@ -86,7 +86,13 @@ typedef struct {
 /* Hyper-parameters of a step. lr, beta (momentum), nesterov and ns_steps follow the
  * optimizer's constructor on the pages; (a, b, c) are the quintic's coefficients; eps guards
  * the normalisation of an all-zero update. ns_steps may be 0 (O = U / (||U||_F + eps)) and
- * is at most 64. Every float must be finite; eps >= 0. */
+ * is at most 64. Every float must be finite; eps >= 0.
+ *
+ * schedule: NULL (every round uses (a, b, c)), or a host array of ns_steps triples
+ * {a_k, b_k, c_k}, k = 0..ns_steps-1, one quintic per round: the mechanism behind the record
+ * analysed at lqnn.cn (section 3.2), which replaces the fixed quintic by a cascade of
+ * re-derived quintic maps (the pages do not print their values, so they are the caller's).
+ * The array is read during the call only; every value must be finite. */
 typedef struct {
   float lr;
   float beta;
@@ -94,10 +100,11 @@ typedef struct {
   int ns_steps;
   float a, b, c;
   float eps;
+  const float *schedule;
 } muon_config;
 
 /* Fills cfg with lr 0.02, beta 0.95, nesterov 1, ns_steps 5, (3.4445, -4.7750, 2.0315),
- * eps 1e-7. A NULL cfg is ignored. */
+ * eps 1e-7, schedule NULL. A NULL cfg is ignored. */
 void muon_config_default(muon_config *cfg);
 
 /* Builds a plan for n matrices (n >= 0) of the given shapes and dtypes. The plan groups the

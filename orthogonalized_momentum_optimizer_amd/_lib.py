@@ -64,6 +64,7 @@ class muon_config(ctypes.Structure):
         ("b", ctypes.c_float),
         ("c", ctypes.c_float),
         ("eps", ctypes.c_float),
+        ("schedule", ctypes.POINTER(ctypes.c_float)),
     ]
 
 

@@ -94,6 +94,10 @@ int check_cfg(const muon_config* cfg, bool momentum) {
     return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (momentum && (!finite(cfg->lr) || !finite(cfg->beta)))
     return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
+  if (cfg->schedule)
+    for (int k = 0; k < 3 * cfg->ns_steps; ++k)
+      if (!finite(cfg->schedule[k]))
+        return fail(MUON_ERR_INVALID_ARG, "schedule entry %d is not finite", k);
   return MUON_OK;
 }
 
@@ -227,14 +231,15 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
       N.x_in = xin;
       N.x_out = xout;
       N.first = r == 0;
+      const float* abc = cfg->schedule ? cfg->schedule + 3 * r : &cfg->a;
+      const float ca = abc[0], cb = abc[1], cc = abc[2];
       L.run(MUON_KERNEL_GRAM, "gram",
             [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(N, stream); });
       L.run(MUON_KERNEL_POLY, "poly", [&] {
-        return f32 ? launch_poly_f32(N, cfg->b, cfg->c, stream)
-                   : launch_poly_bf16(N, cfg->a, cfg->b, cfg->c, stream);
+        return f32 ? launch_poly_f32(N, cb, cc, stream) : launch_poly_bf16(N, ca, cb, cc, stream);
       });
       L.run(MUON_KERNEL_APPLY, "apply", [&] {
-        return f32 ? launch_apply_f32(N, cfg->a, stream) : launch_apply_bf16(N, stream);
+        return f32 ? launch_apply_f32(N, ca, stream) : launch_apply_bf16(N, stream);
       });
       std::swap(xin, xout);
     }
@@ -285,6 +290,7 @@ void muon_config_default(muon_config* cfg) {
   cfg->b = -4.7750f;
   cfg->c = 2.0315f;
   cfg->eps = 1e-7f;
+  cfg->schedule = nullptr;
 }
 
 int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,

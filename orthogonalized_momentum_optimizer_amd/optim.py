@@ -10,6 +10,7 @@ runs entirely in libmuon.so.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import List, Optional, Sequence
 
 import torch
@@ -27,11 +28,19 @@ def dtype_code(dt: torch.dtype) -> int:
 
 
 def make_config(lr=0.02, beta=0.95, nesterov=True, ns_steps=5, abc=(3.4445, -4.7750, 2.0315),
-                eps=1e-7) -> L.muon_config:
+                eps=1e-7, schedule=None) -> L.muon_config:
+    """A muon_config. ``schedule``: None, or ns_steps (a, b, c) triples, one per round."""
     cfg = L.muon_config_default()
     cfg.lr, cfg.beta, cfg.nesterov, cfg.ns_steps = lr, beta, int(bool(nesterov)), int(ns_steps)
     cfg.a, cfg.b, cfg.c = abc
     cfg.eps = eps
+    if schedule is not None:
+        flat = [float(x) for triple in schedule for x in triple]
+        if len(flat) != 3 * int(ns_steps):
+            raise ValueError("schedule must hold ns_steps (a, b, c) triples")
+        arr = (ctypes.c_float * max(len(flat), 1))(*flat)
+        cfg.schedule = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+        cfg._schedule_keepalive = arr   # the array lives as long as the config
     return cfg
 
 

@@ -199,6 +199,27 @@ def test_step_rejects_config(field, value):
 
 
 @no_gpu_only
+def test_step_rejects_non_finite_schedule():
+    from orthogonalized_momentum_optimizer_amd import make_config
+    good = make_config(ns_steps=2, schedule=[(3.4445, -4.775, 2.0315), (1.875, -1.25, 0.375)])
+    bad = make_config(ns_steps=2, schedule=[(3.4445, -4.775, 2.0315), (1.875, float("nan"), 0.375)])
+    status, msg = _fake_call(cfg_mut=lambda c: setattr(c, "schedule", bad.schedule))
+    assert status == L.MUON_ERR_INVALID_ARG and "schedule" in msg
+    status, msg = _fake_call(cfg_mut=lambda c: (setattr(c, "schedule", good.schedule),
+                                                setattr(c, "ns_steps", 2)))
+    assert status == L.MUON_ERR_HIP, msg     # passes validation, fails only at launch
+
+
+def test_make_config_schedule_length():
+    from orthogonalized_momentum_optimizer_amd import make_config
+    with pytest.raises(ValueError):
+        make_config(ns_steps=3, schedule=[(1.0, 0.0, 0.0)] * 2)
+    cfg = make_config(ns_steps=2, schedule=[(1.0, 2.0, 3.0), (4.0, 5.0, 6.0)])
+    assert [cfg.schedule[k] for k in range(6)] == [1.0, 2.0, 3.0, 4.0, 5.0, 6.0]
+    assert not make_config().schedule
+
+
+@no_gpu_only
 def test_step_rejects_workspace():
     assert _fake_call(ws_off=16)[0] == L.MUON_ERR_WORKSPACE
     assert _fake_call(ws_bytes=1024)[0] == L.MUON_ERR_WORKSPACE
