@@ -15,6 +15,8 @@
 //    distinct 16-byte bank groups.
 #pragma once
 
+#include <utility>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -123,6 +125,33 @@ __device__ __forceinline__ u32x4 ds_read_b128(const u32x4* p) {
   u32x4 r;
   asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
   return r;
+}
+
+// The same reads from a byte address in LDS plus a compile-time offset (the instruction's
+// 16-bit offset field), so that a run of reads shares one address register.
+template <int OFF>
+__device__ __forceinline__ s16x4 ds_read_tr_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0..N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Waits for this wave's LDS reads; ties the fragments to the wait so no use moves above it.

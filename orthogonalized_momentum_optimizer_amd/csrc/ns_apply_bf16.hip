@@ -8,8 +8,11 @@
 // with a scaling epilogue and no second operand to read. s1 = 1/nu on the first round (the
 // Frobenius normalisation folded in), else 1.
 //
-// Tiling: 256 threads (4 waves as 2x2), a 256x256 output tile per block, each wave 128x128
-// as 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs).
+// Tiling: 256 threads (4 waves as 2x2), a 256x256 output tile per block, each wave 128 rows
+// (wr) by four 32-column blocks at 64j + 32wc, as 4x4 v_mfma_f32_32x32x16_bf16 blocks (256
+// fp32 accumulators per lane, in AGPRs). Interleaving the waves' column blocks keeps each
+// wave's LDS read addresses a fixed immediate offset apart (see the kernel's set-up), so
+// the inner loop spends no vector instructions on addressing.
 // Per flop this moves half the global and LDS bytes of a 128x128 tile. K advances 32 at a
 // time through a ring of 4 LDS stages of 32 KB (one block per CU, one wave per SIMD), so
 // the loop is an explicit software pipeline (below). The left operand B' is
@@ -41,11 +44,35 @@ struct ApplyArgs {
   int tiles_m, tiles_n, total_tiles;
 };
 
+// Fragments of one 16-wide K slice: 8 transposed half-fragments of the right operand and 4
+// fragments of the left.
+struct Frags {
+  s16x4 bh[4][2];
+  u32x4 av[4];
+};
+
+// LDS read `OP` of K slice `KS`: ops 0-7 are the transposing reads of right-operand
+// fragment OP/2, half OP%2; ops 8-11 the left-operand fragments. `va` is the lane's
+// left-operand address for slice KS of the stage and `vb` its right-operand address; every
+// other read of the stage is a fixed offset from those (see the kernel's set-up).
+template <int KS, int OP>
+__device__ __forceinline__ void lds_op(uint32_t va, uint32_t vb, Frags& f) {
+  if constexpr (OP < 8) {
+    constexpr int j = OP >> 1, half = OP & 1;
+    f.bh[j][half] = ds_read_tr_at<128 * j + 2 * 4 * TN * half + 2 * 16 * TN * KS>(vb);
+  } else {
+    constexpr int i = OP - 8;
+    f.av[i] = ds_read_b128_at<2 * 32 * TK * i>(va);
+  }
+}
+
 __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  // wave-uniform, so every LDS destination of the direct loads is scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
   const int L = xcd_remap(blockIdx.x, g.total_tiles);
@@ -55,8 +82,9 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   const int I = tt / g.tiles_n, J = tt - (tt / g.tiles_n) * g.tiles_n;
 
   const size_t mm = (size_t)g.mp * g.mp, mn = (size_t)g.mp * g.np;
-  const uint16_t* lhs = g.b + bidx * mm;
-  const uint16_t* rhs = g.x + bidx * mn;
+  const char* lhs = reinterpret_cast<const char*>(g.b + bidx * mm);
+  const char* rhs = reinterpret_cast<const char*>(g.x + bidx * mn);
+  const size_t rhs_stage_bytes = (size_t)2 * TK * g.np;
   const int row0 = I * TM, col0 = J * TN;
 
   f32x16 acc[4][4];
@@ -69,49 +97,56 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
 
   const int KT = g.mp / TK;
 
-  // ---- memory operations, one instruction each, so they can be interleaved with MFMAs ----
-  // Direct-to-LDS loads of stage kt: ops 0-3 fetch left-operand rows, 4-7 right-operand rows.
+  // ---- direct-to-LDS loads: 8 per wave per stage, one instruction each ----
+  // Loads 0-3 fetch 16 left-operand rows each (4 lanes x 16 bytes per row), loads 4-7 two
+  // right-operand K-rows each (32 lanes x 16 bytes per row); lane l lands at 16 l of a 1 KB
+  // LDS block, so the swizzle is applied by choosing the global chunk a lane fetches. The
+  // global address is a wave-uniform base (the operand's stage origin, in scalar registers)
+  // plus the lane's 32-bit byte offset below, fixed for the whole loop.
+  uint32_t doff[8];
+#pragma unroll
+  for (int op = 0; op < 4; ++op) {
+    const int row = 16 * (4 * wave + op) + (lane >> 2);
+    const int c = (lane & 3) ^ kswz(row);
+    const uint32_t grow = min(row0 + row, g.mp - 1);
+    doff[op] = 2u * (grow * (uint32_t)g.mp + 8u * c);
+  }
+#pragma unroll
+  for (int op = 0; op < 4; ++op) {
+    const int k = 2 * (4 * wave + op) + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (k & 3));
+    const uint32_t gcol = min(col0 + 8 * c, g.np - 8);
+    doff[4 + op] = 2u * ((uint32_t)k * (uint32_t)g.np + gcol);
+  }
   auto dma_op = [&](int kt, int op) {
-    u32x4* st = smem + (kt % NSTAGE) * kUnitsStage;
-    if (op < 4) {
-      const int blk = 4 * wave + op;
-      const int row = 16 * blk + (lane >> 2);
-      const int c = (lane & 3) ^ kswz(row);
-      const int grow = min(row0 + row, g.mp - 1);
-      __builtin_amdgcn_global_load_lds(lhs + (size_t)grow * g.mp + kt * TK + 8 * c,
-                                       MUON_LDS_PTR(st + 64 * blk), 16, 0, 0);
-    } else {
-      const int blk = 4 * wave + (op - 4);
-      const int k = 2 * blk + (lane >> 5);
-      const int c = (lane & 31) ^ (2 * (k & 3));
-      const int gcol = min(col0 + 8 * c, g.np - 8);
-      __builtin_amdgcn_global_load_lds(rhs + (size_t)(kt * TK + k) * g.np + gcol,
-                                       MUON_LDS_PTR(st + kUnitsA + 64 * blk), 16, 0, 0);
-    }
+    u32x4* st = smem + (kt & (NSTAGE - 1)) * kUnitsStage;
+    if (op < 4)
+      __builtin_amdgcn_global_load_lds(lhs + (size_t)kt * (2 * TK) + doff[op],
+                                       MUON_LDS_PTR(st + 64 * (4 * wave + op)), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(rhs + (size_t)kt * rhs_stage_bytes + doff[op],
+                                       MUON_LDS_PTR(st + kUnitsA + 64 * (4 * wave + op - 4)),
+                                       16, 0, 0);
   };
-  // LDS reads of one 16-wide K slice (ks) of stage kt: ops 0-7 are the transposing reads of
-  // the right-operand fragments (fragment op/2, half op%2), ops 8-11 the left fragments.
-  struct Frags {
-    s16x4 bh[4][2];
-    u32x4 av[4];
-  };
-  auto lds_op = [&](int kt, int ks, int op, Frags& f) {
-    const u32x4* A = smem + (kt % NSTAGE) * kUnitsStage;
-    if (op < 8) {
-      const int j = op >> 1, half = op & 1;
-      const int grp = lane >> 4, jj = lane & 15;
-      const int n = wc * 128 + j * 32 + 16 * (grp & 1) + 4 * (jj & 3);
-      const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (jj >> 2);
-      const int c = (n >> 3) ^ (2 * (k & 3));
-      f.bh[j][half] = ds_read_tr(reinterpret_cast<const uint16_t*>(A + kUnitsA) + k * TN + 8 * c +
-                                 (n & 7));
-    } else {
-      const int i = op - 8;
-      const int row = wr * 128 + i * 32 + (lane & 31);
-      const int c = 2 * ks + (lane >> 5);
-      f.av[i] = ds_read_b128(A + row * 4 + (c ^ kswz(row)));
-    }
-  };
+
+  // ---- LDS read addresses ----
+  // Left fragment i of slice ks: row wr*128 + 32i + l%32, chunk 2ks + l/32 (swizzled by
+  // bits 2-3 of the row, which 32i leaves alone): base aoff[ks] plus 2048 i bytes.
+  // Right fragment j, half h of slice ks: columns 64j + 32wc + (16-column group) of K-rows
+  // 16ks + 8(group/2) + 4h + 0..3. Fragment j of a wave covers columns 64j + 32wc, so j
+  // moves the chunk index by 8j, above the bits the row swizzle (chunk ^ 2(k & 3)) changes,
+  // and h, ks move whole groups of 4 rows, leaving k & 3 alone: base boff plus
+  // 128 j + 2048 h + 8192 ks bytes.
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MUON_LDS_PTR(smem)));
+  const int arow = wr * 128 + (lane & 31);
+  const uint32_t aoff0 = 64 * arow + 16 * ((lane >> 5) ^ kswz(arow));
+  const uint32_t aoff1 = 64 * arow + 16 * ((2 + (lane >> 5)) ^ kswz(arow));
+  const int grp = lane >> 4, jj = lane & 15;
+  const int bn = 32 * wc + 16 * (grp & 1) + 4 * (jj & 3);
+  const int bk = 8 * (grp >> 1) + (jj >> 2);
+  const uint32_t boff = 16 * kUnitsA + 2 * (bk * TN + 8 * ((bn >> 3) ^ (2 * (bk & 3))) + (bn & 7));
+  auto stage_base = [&](int kt) { return lds0 + (uint32_t)((kt & (NSTAGE - 1)) * kUnitsStage * 16); };
+
   // Waits for the reads of `f` (and every earlier LDS read of this wave), then assembles the
   // MFMA operands; the assembly depends on the wait, so it cannot move above it.
   auto ready = [&](Frags& f, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
@@ -148,44 +183,53 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   // of slice 1 are issued between its MFMAs; then (slice 1 in registers, so this wave is done
   // with the stage) the next stage's barrier; while batch 1 runs, the 8 direct loads of stage
   // kt + 4 (into this stage's buffer) and the 12 reads of the next stage's slice 0 are issued
-  // between its MFMAs. sched_barrier fences pin that order.
-#pragma unroll
-  for (int s = 0; s < NSTAGE; ++s)
-    if (s < KT)
-      for (int op = 0; op < 8; ++op) dma_op(s, op);
-  stage_ready(min(NSTAGE - 1, KT - 1));
+  // between its MFMAs. sched_barrier fences pin that order. The stage loop is split where
+  // the refills stop and before the last stage, so neither condition is a branch inside it.
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   Frags f0, f1;
-#pragma unroll
-  for (int op = 0; op < 12; ++op) lds_op(0, 0, op, f0);
-  ready(f0, a0, b0);
-
-  for (int kt = 0; kt < KT; ++kt) {
+  auto iteration = [&](int kt, auto refill_t, auto more_t) {
+    constexpr bool refill = decltype(refill_t)::value, more = decltype(more_t)::value;
+    const uint32_t cur = stage_base(kt);
+    const uint32_t va1 = cur + aoff1, vb = cur + boff;
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    static_for<16>([&](auto M) {
+      constexpr int m = decltype(M)::value;
       mfma(m, a0, b0);
       __builtin_amdgcn_sched_barrier(0);
-      if (m < 12) lds_op(kt, 1, m, f1);
+      if constexpr (m < 12) lds_op<1, m>(va1, vb, f1);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     ready(f1, a1, b1);  // slice 1 is in registers: this wave is done reading stage kt
-    const bool more = kt + 1 < KT;
-    if (more) stage_ready(min(NSTAGE - 2, KT - 2 - kt));
-    const bool refill = kt + NSTAGE < KT;
+    if constexpr (more) {
+      if constexpr (refill) stage_ready(NSTAGE - 2);
+      else stage_ready(min(NSTAGE - 2, KT - 2 - kt));
+    }
+    const uint32_t nxt = stage_base(kt + 1);
+    const uint32_t va0n = nxt + aoff0, vbn = nxt + boff;
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    static_for<16>([&](auto M) {
+      constexpr int m = decltype(M)::value;
       mfma(m, a1, b1);
       __builtin_amdgcn_sched_barrier(0);
-      if (m < 8) {
-        if (refill) dma_op(kt + NSTAGE, m);
-      }
-      if (more && m >= 2 && m < 14) lds_op(kt + 1, 0, m - 2, f0);
+      if constexpr (refill && m < 8) dma_op(kt + NSTAGE, m);
+      if constexpr (more && m >= 2 && m < 14) lds_op<0, m - 2>(va0n, vbn, f0);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) ready(f0, a0, b0);
-  }
+    });
+    if constexpr (more) ready(f0, a0, b0);
+  };
+
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st)
+#pragma unroll
+    for (int op = 0; op < 8; ++op) dma_op(st, op);  // KT >= 4: mp is a multiple of 128
+  stage_ready(NSTAGE - 1);
+  static_for<12>([&](auto OP) { lds_op<0, decltype(OP)::value>(lds0 + aoff0, lds0 + boff, f0); });
+  ready(f0, a0, b0);
+
+  int kt = 0;
+  for (; kt < KT - NSTAGE; ++kt) iteration(kt, std::true_type{}, std::true_type{});
+  for (; kt < KT - 1; ++kt) iteration(kt, std::false_type{}, std::true_type{});
+  iteration(KT - 1, std::false_type{}, std::false_type{});
 
   // Epilogue: scale, round to bf16 and stage the 256x256 tile in LDS (128 KB, the whole
   // operand ring), then store 16-byte chunks with 32 lanes per 512-byte row segment; stores
@@ -203,7 +247,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = wc * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        const int col = 64 * j + 32 * wc + 8 * q + 4 * (lane >> 5);
         u32x2 w;
         w.x = pack_bf16(acc[i][j][4 * q] * s, acc[i][j][4 * q + 1] * s);
         w.y = pack_bf16(acc[i][j][4 * q + 2] * s, acc[i][j][4 * q + 3] * s);
