@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
   __shared__ u32x4 smem[STAGES * kStage];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  // wave-uniform, so every LDS destination of the direct loads is scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
   const int L = xcd_remap(blockIdx.x, g.total_tiles);
@@ -99,26 +101,47 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = g.K / BK;
+  const int KT = g.K / BK;  // >= 4: K is a multiple of 128
+
+  // Direct-to-LDS loads, 4 per wave per stage: loads 0-1 fetch 16 rows each of the left
+  // tile (rows of block I), loads 2-3 of the right tile (block J); 4 lanes x 16 bytes per
+  // row, lane l landing at 16 l of a 1 KB LDS block (the K-major swizzle is applied by the
+  // global chunk a lane fetches). Rows at or beyond mp are fetched from row mp - 1 (their
+  // products are never stored). The global address is the stage's K origin (scalar) plus the
+  // lane's fixed 32-bit byte offset.
+  const char* srcb = reinterpret_cast<const char*>(src);
+  uint32_t doff[4];
+#pragma unroll
+  for (int op = 0; op < 4; ++op) {
+    const int row = 16 * (2 * wave + (op & 1)) + (lane >> 2);
+    const int c = (lane & 3) ^ kswz(row);
+    const uint32_t grow = min((op < 2 ? I * BM : J * BN) + row, g.mp - 1);
+    doff[op] = 2u * (grow * (uint32_t)g.ld_in + 8u * c);
+  }
   auto issue = [&](int kt) {
-    u32x4* st = smem + (kt % STAGES) * kStage;
-    dma_kmajor<BM, 4>(src, g.ld_in, I * BM, g.mp, kt * BK, st);
-    dma_kmajor<BN, 4>(src, g.ld_in, J * BN, g.mp, kt * BK, st + 512);
+    u32x4* st = smem + (kt & (STAGES - 1)) * kStage;
+    const char* base = srcb + (size_t)kt * (2 * BK);
+#pragma unroll
+    for (int op = 0; op < 4; ++op)
+      __builtin_amdgcn_global_load_lds(base + doff[op],
+                                       MUON_LDS_PTR(st + (op < 2 ? 0 : 512) +
+                                                    64 * (2 * wave + (op & 1))),
+                                       16, 0, 0);
   };
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wave's loads of stage kt are done once at most the later stages' are pending
-    const int later = min(STAGES - 2, KT - 1 - kt);
-    if (later >= 2) vm_wait<2 * kLoadsPerStage>();
-    else if (later == 1) vm_wait<kLoadsPerStage>();
-    else vm_wait<0>();
+  // One stage of the main loop. LATER: this wave's loads issued after stage kt's (two
+  // stages while refills run, then one, then none), so stage kt is in once at most LATER
+  // stages' loads are pending; REFILL: whether stage kt + 3 is loaded into the buffer that
+  // every wave finished with before this stage's barrier.
+  auto stage = [&](int kt, auto later_t, auto refill_t) {
+    constexpr int later = decltype(later_t)::value;
+    vm_wait<later * kLoadsPerStage>();
     // every wave's loads of stage kt are visible, and every wave is done with stage kt - 1
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    if constexpr (decltype(refill_t)::value) issue(kt + STAGES - 1);
 
     const u32x4* A = smem + (kt % STAGES) * kStage;
     const u32x4* B = A + 512;
@@ -143,7 +166,15 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-  }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int kt = 0;
+  for (; kt < KT - (STAGES - 1); ++kt) stage(kt, I2{}, std::true_type{});
+  stage(kt++, I2{}, std::false_type{});
+  stage(kt++, I1{}, std::false_type{});
+  stage(kt, I0{}, std::false_type{});
   // all waves are done reading the operand stages before the epilogue reuses them
   __syncthreads();
 
