@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip"]
+SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -74,6 +74,26 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def device_asm(src: str) -> str:
+    """Compiles one source under csrc/ to gfx950 assembly (device code only, the library's
+    flags) into _build/asm/ and returns the path; reused while the source files are unchanged."""
+    import hashlib
+    out_dir = os.path.join(BUILD, "asm")
+    os.makedirs(out_dir, exist_ok=True)
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)) + [os.path.join(INCLUDE, "muon.h")]:
+        path = name if os.path.isabs(name) else os.path.join(CSRC, name)
+        with open(path, "rb") as f:
+            h.update(f.read())
+    out = os.path.join(out_dir, f"{os.path.splitext(src)[0]}-{h.hexdigest()[:16]}.s")
+    if not os.path.exists(out):
+        tmp = out + ".tmp"
+        _run([hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src),
+              "-o", tmp])
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -53,6 +53,11 @@ struct NsGroup {
 };
 // bf16 storage, bf16 matrix cores with fp32 accumulation (ns_gemm_bf16.hip, ns_apply_bf16.hip).
 // The bf16 round folds a I into B: poly writes B' = aI + bA + cAA and apply forms s1 B' X.
+// 256x256-tile versions of gram and poly (ns_sym256_bf16.hip); the two launchers below hand
+// a shape group to them when use_sym256(g).
+bool use_sym256(const NsGroup& g);
+hipError_t launch_gram256_bf16(const NsGroup& g, hipStream_t s);
+hipError_t launch_poly256_bf16(const NsGroup& g, float a, float b, float c, hipStream_t s);
 hipError_t launch_gram_bf16(const NsGroup& g, hipStream_t s);   // A = s2 X X^T
 hipError_t launch_poly_bf16(const NsGroup& g, float a, float b, float c,
                             hipStream_t s);                     // B' = aI + bA + cAA

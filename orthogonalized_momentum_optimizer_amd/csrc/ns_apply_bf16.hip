@@ -240,21 +240,28 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   const float s = g.scales ? g.scales[4 * bidx] : 1.f;
   __syncthreads();  // every wave is done with the operand stages
   u32x2* st2 = reinterpret_cast<u32x2*>(smem);  // 8-byte units: row * 64 + 2 * chunk + half
+  // the scale is 1 after the first round: skip its 256 multiplies per lane there
+  auto stage_out = [&](auto scaled_t) {
+    constexpr bool scaled = decltype(scaled_t)::value;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wr * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < 4; ++i) {
+      const int row = wr * 128 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 64 * j + 32 * wc + 8 * q + 4 * (lane >> 5);
-        u32x2 w;
-        w.x = pack_bf16(acc[i][j][4 * q] * s, acc[i][j][4 * q + 1] * s);
-        w.y = pack_bf16(acc[i][j][4 * q + 2] * s, acc[i][j][4 * q + 3] * s);
-        st2[row * 64 + 2 * ((col >> 3) ^ (row & 15)) + ((col >> 2) & 1)] = w;
+        for (int q = 0; q < 4; ++q) {
+          const int col = 64 * j + 32 * wc + 8 * q + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = scaled ? acc[i][j][4 * q + e] * s : acc[i][j][4 * q + e];
+          st2[row * 64 + 2 * ((col >> 3) ^ (row & 15)) + ((col >> 2) & 1)] =
+              u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
       }
     }
-  }
+  };
+  if (g.scales) stage_out(std::true_type{});
+  else stage_out(std::false_type{});
   __syncthreads();
   uint16_t* out = g.out + bidx * mn;
   const int ch = t & 31;

@@ -269,6 +269,7 @@ SymArgs sym_args(const NsGroup& G) {
 }  // namespace
 
 hipError_t launch_gram_bf16(const NsGroup& G, hipStream_t s) {
+  if (use_sym256(G)) return launch_gram256_bf16(G, s);
   SymArgs a = sym_args(G);
   a.in = static_cast<const uint16_t*>(G.x_in);
   a.out = static_cast<uint16_t*>(G.a);
@@ -281,6 +282,7 @@ hipError_t launch_gram_bf16(const NsGroup& G, hipStream_t s) {
 }
 
 hipError_t launch_poly_bf16(const NsGroup& G, float ca, float cb, float cc, hipStream_t s) {
+  if (use_sym256(G)) return launch_poly256_bf16(G, ca, cb, cc, s);
   SymArgs a = sym_args(G);
   a.in = static_cast<const uint16_t*>(G.a);
   a.out = static_cast<uint16_t*>(G.b);

@@ -37,6 +37,18 @@ def test_ragged_shapes_fp32_params(precision):
     compare(wl, gpu, 2, precision)
 
 
+@pytest.mark.parametrize("precision", ["bf16"])
+def test_large_tile_products_ragged(precision):
+    """Shape groups with mp >= 512 use 256x256 tiles for the Gram and polynomial products:
+    mp = 640 leaves the last tile row half outside the matrix, 512 is exactly two tiles, and
+    the tall 1000x530 runs transposed (mp 640, np 1024)."""
+    _announce(f"256-tile products {precision}")
+    wl = si.custom([(640, 640), (600, 1000), (1000, 530), (512, 512), (512, 1536)],
+                   cfg_id=111, steps=2)
+    gpu = run_gpu(wl, 2, precision)
+    compare(wl, gpu, 2, precision)
+
+
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_gpt2_tiny_fp32_workload(precision):
     """64x256 fp32 matrix, one N(0,1) gradient reused for 3 steps."""
