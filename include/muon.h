@@ -121,13 +121,7 @@ int muon_plan_create(muon_plan **out, const int64_t *rows, const int64_t *cols,
  * not be preserved between calls. Returns 0 for a NULL plan. */
 size_t muon_plan_workspace_size(const muon_plan *plan);
 
-/* One Muon step over mats[0..n-1]; n must equal the plan's count (n = 0 is a no-op).
- * With more than one shape group, each group's launches run on one of up to 4 internal
- * streams of the plan, forked from `stream` at the start of the call and joined back into it
- * at the end (events only: the call still returns without synchronising, and work enqueued
- * on `stream` afterwards waits for the whole step). The first such call on a device creates
- * those streams and events there (a HIP resource allocation, no device memory); later calls
- * reuse them, and muon_plan_destroy releases them. Both entry points behave this way. */
+/* One Muon step over mats[0..n-1]; n must equal the plan's count (n = 0 is a no-op). */
 int muon_step(muon_plan *plan, const muon_matrix *mats, int64_t n, const muon_config *cfg,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -143,9 +137,8 @@ void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
 
 /* Kernel timing for measurement. When enabled, every later muon_step/muon_newton_schulz
  * records a HIP event pair around each kernel launch on the call's stream (events are
- * created here, on the current device; the step itself still allocates nothing), and runs
- * every launch in order on that stream (no concurrency between shape groups), so each
- * kernel's time is its own. Enabling resets the totals; disabling releases the events. */
+ * created here, on the current device; the step itself still allocates nothing). Enabling
+ * resets the totals; disabling releases the events. */
 int muon_plan_set_profiling(muon_plan *plan, int enable);
 
 /* Kinds of kernel, in the order of a step. */

@@ -53,6 +53,39 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return (x < r) ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
+// One grid over the tiles of several shape groups. The groups are given longest tiles first;
+// each XCD receives an even share of every group (q tiles, plus one of the group's r left
+// over, dealt round robin over the XCDs continuing from the previous group's), contiguous
+// within the group so that one XCD's L2 serves the matrices it works on, and an XCD takes
+// its share of the first (longest) group first. Block ids reach the XCDs round robin
+// (id % 8), in increasing order on each XCD.
+constexpr int kMaxLaunchGroups = 8;
+struct TileSplit {
+  int n;                        // groups in the launch
+  int q[kMaxLaunchGroups];      // tiles / 8
+  int r[kMaxLaunchGroups];      // tiles % 8
+  int off[kMaxLaunchGroups];    // first XCD of the group's left-over tiles
+};
+
+// Group of block `b` (returned) and the tile index within that group.
+__device__ __forceinline__ int split_block(int b, const TileSplit& ts, int& tile) {
+  const int x = b & 7;
+  int s = b >> 3;
+  for (int g = 0; g < ts.n; ++g) {
+    const int q = ts.q[g], r = ts.r[g], off = ts.off[g];
+    const int cnt = q + (((x - off) & 7) < r ? 1 : 0);
+    if (s < cnt) {
+      int before = 0;
+      for (int y = 0; y < x; ++y) before += ((y - off) & 7) < r ? 1 : 0;
+      tile = x * q + before + s;
+      return g;
+    }
+    s -= cnt;
+  }
+  tile = 0;
+  return 0;  // not reached: the grid is the groups' total tile count
+}
+
 // vmcnt <= N for this wave's outstanding vector-memory loads (lgkm and exp unconstrained).
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -51,17 +51,20 @@ struct NsGroup {
   int batch, mp, np;
   int first;           // first round: fold the 1/nu normalisation into the epilogues
 };
-// bf16 storage, bf16 matrix cores with fp32 accumulation (ns_gemm_bf16.hip, ns_apply_bf16.hip).
-// The bf16 round folds a I into B: poly writes B' = aI + bA + cAA and apply forms s1 B' X.
-// 256x256-tile versions of gram and poly (ns_sym256_bf16.hip); the two launchers below hand
-// a shape group to them when use_sym256(g).
+// bf16 storage, bf16 matrix cores with fp32 accumulation. The bf16 round folds a I into B:
+// poly writes B' = aI + bA + cAA and apply forms s1 B' X. Each launcher takes one or more
+// shape groups of a round (the step passes one group at a time): groups with use_sym256
+// (mp >= 1024) share 256x256-tile launches (one per 8 groups, ns_sym256_bf16.hip; apply
+// always, ns_apply_bf16.hip), tiles ordered longest first on every XCD; smaller groups use
+// 128x128 tiles, one launch each (ns_gemm_bf16.hip).
 bool use_sym256(const NsGroup& g);
-hipError_t launch_gram256_bf16(const NsGroup& g, hipStream_t s);
-hipError_t launch_poly256_bf16(const NsGroup& g, float a, float b, float c, hipStream_t s);
-hipError_t launch_gram_bf16(const NsGroup& g, hipStream_t s);   // A = s2 X X^T
-hipError_t launch_poly_bf16(const NsGroup& g, float a, float b, float c,
-                            hipStream_t s);                     // B' = aI + bA + cAA
-hipError_t launch_apply_bf16(const NsGroup& g, hipStream_t s);  // X' = s1 B' X
+hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s);   // A = s2 X X^T
+hipError_t launch_poly_bf16(const NsGroup* groups, int n, float a, float b, float c,
+                            hipStream_t s);                                 // B' = aI+bA+cAA
+hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s);  // X' = s1 B' X
+hipError_t launch_gram256_bf16(const NsGroup* groups, int n, hipStream_t s);
+hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, float c,
+                               hipStream_t s);
 // fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip): B = bA + cAA and
 // X' = s1 (aX + BX), the round as written
 hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);

@@ -23,6 +23,8 @@
 // stages of 16 KB (64 KB per block, two blocks per CU), filled with direct-to-LDS loads three
 // stages ahead. Both operands are K-contiguous (rows of X, rows of A; layouts in
 // mfma_common.h).
+#include <vector>
+
 #include "mfma_common.h"
 
 namespace muon {
@@ -268,8 +270,9 @@ SymArgs sym_args(const NsGroup& G) {
 
 }  // namespace
 
-hipError_t launch_gram_bf16(const NsGroup& G, hipStream_t s) {
-  if (use_sym256(G)) return launch_gram256_bf16(G, s);
+namespace {
+
+hipError_t launch_gram128(const NsGroup& G, hipStream_t s) {
   SymArgs a = sym_args(G);
   a.in = static_cast<const uint16_t*>(G.x_in);
   a.out = static_cast<uint16_t*>(G.a);
@@ -281,8 +284,7 @@ hipError_t launch_gram_bf16(const NsGroup& G, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_poly_bf16(const NsGroup& G, float ca, float cb, float cc, hipStream_t s) {
-  if (use_sym256(G)) return launch_poly256_bf16(G, ca, cb, cc, s);
+hipError_t launch_poly128(const NsGroup& G, float ca, float cb, float cc, hipStream_t s) {
   SymArgs a = sym_args(G);
   a.in = static_cast<const uint16_t*>(G.a);
   a.out = static_cast<uint16_t*>(G.b);
@@ -294,6 +296,30 @@ hipError_t launch_poly_bf16(const NsGroup& G, float ca, float cb, float cc, hipS
   a.c = cc;
   hipLaunchKernelGGL(ns_sym_bf16<POLY>, dim3(a.total_tiles), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Groups with use_sym256 go to the 256-tile kernel together (ns_sym256_bf16.hip); the rest
+// run here, one launch per group.
+hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s) {
+  std::vector<NsGroup> big;
+  for (int i = 0; i < n; ++i) {
+    if (use_sym256(groups[i])) big.push_back(groups[i]);
+    else if (hipError_t e = launch_gram128(groups[i], s)) return e;
+  }
+  return big.empty() ? hipSuccess : launch_gram256_bf16(big.data(), (int)big.size(), s);
+}
+
+hipError_t launch_poly_bf16(const NsGroup* groups, int n, float ca, float cb, float cc,
+                            hipStream_t s) {
+  std::vector<NsGroup> big;
+  for (int i = 0; i < n; ++i) {
+    if (use_sym256(groups[i])) big.push_back(groups[i]);
+    else if (hipError_t e = launch_poly128(groups[i], ca, cb, cc, s)) return e;
+  }
+  return big.empty() ? hipSuccess
+                     : launch_poly256_bf16(big.data(), (int)big.size(), ca, cb, cc, s);
 }
 
 }  // namespace muon

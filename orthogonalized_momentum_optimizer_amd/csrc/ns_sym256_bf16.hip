@@ -2,7 +2,7 @@
 //
 // Same products as ns_gemm_bf16.hip (page "深入解析KellerJordan/modded-nanogpt中的训练架构与
 // 优化技术", section "Newton-Schulz正交化": A = X X^T, B = b A + c A A), for shape groups
-// with mp >= 512:
+// with mp >= 1024 (use_sym256 below):
 //
 //   gram   A  = s2 * X X^T              K = np
 //   poly   B' = a I + b A + c A A       K = mp   (A A = A A^T since A is symmetric)
@@ -21,6 +21,9 @@
 // from its rows and its lower triangle from the transpose, so A and B' are exactly
 // symmetric. POLY's b A term is the tile A[I-tile][J-tile], loaded into the ring by the last
 // iterations of the K loop and combined in fp32 before the rounding.
+#include <algorithm>
+#include <vector>
+
 #include "mfma_common.h"
 
 namespace muon {
@@ -35,14 +38,19 @@ constexpr int kLoadsPerStage = 8;              // direct loads per wave per stag
 
 enum Mode { GRAM = 0, POLY = 1 };
 
-struct Sym256Args {
+struct Sym256Args {     // one shape group
   const uint16_t* in;   // GRAM: X (batch x mp x np); POLY: A (batch x mp x mp)
   uint16_t* out;        // batch x mp x mp
+  const float* scales;  // GRAM first round: per matrix {s1, s2, nu, 0}; else null
   long long in_bs;
   int ld_in, K, mp;
   int tiles;            // tiles per side: ceil(mp / 256)
-  int tiles_per_mat, total_tiles;
-  const float* scales;  // GRAM first round: per matrix {s1, s2, nu, 0}; else null
+  int tiles_per_mat;
+};
+
+struct Sym256Launch {   // the shape groups of one launch, longest tiles (largest K) first
+  TileSplit split;
+  Sym256Args g[kMaxLaunchGroups];
   float a, b, c;        // POLY coefficients
 };
 
@@ -71,7 +79,7 @@ __device__ __forceinline__ uint32_t stage_byte(int row, int col) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Args g) {
+__global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Launch S) {
   __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB
 
   const int t = threadIdx.x;
@@ -79,7 +87,8 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
-  const int L = xcd_remap(blockIdx.x, g.total_tiles);
+  int L;
+  const Sym256Args g = S.g[split_block(blockIdx.x, S.split, L)];
   const int bidx = L / g.tiles_per_mat;
   int tt = L - bidx * g.tiles_per_mat;
   int I = 0;
@@ -248,8 +257,8 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Args g) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t h = (e < 2 ? w.x : w.y) >> (16 * (e & 1));
-            v[e] = fmaf(g.b, bf2f(h & 0xffffu), g.c * acc[i][j][4 * q + e]);
-            if (diag && lr == lc + e) v[e] += g.a;
+            v[e] = fmaf(S.b, bf2f(h & 0xffffu), S.c * acc[i][j][4 * q + e]);
+            if (diag && lr == lc + e) v[e] += S.a;
           }
           pk[i][j][2 * q] = pack_bf16(v[0], v[1]);
           pk[i][j][2 * q + 1] = pack_bf16(v[2], v[3]);
@@ -368,41 +377,66 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Args g) {
 
 }  // namespace
 
-bool use_sym256(const NsGroup& G) { return G.mp >= 512; }
+// The 256-tile kernel moves half the L2 bytes per flop but gives a group a quarter as many
+// tiles: on GPT-2-124M's 768-wide groups (288 and 144 tiles per launch) the 128-tile kernel
+// was measured faster, on GPT-2-1.5B's 1664-wide groups the 256-tile kernel (gram 16.1 vs
+// 18.6 ms per step).
+bool use_sym256(const NsGroup& G) { return G.mp >= 1024; }
 
-static Sym256Args sym256_args(const NsGroup& G) {
-  Sym256Args a{};
-  a.mp = G.mp;
-  a.tiles = (G.mp + TS - 1) / TS;
-  a.tiles_per_mat = a.tiles * (a.tiles + 1) / 2;
-  a.total_tiles = a.tiles_per_mat * G.batch;
-  return a;
+namespace {
+
+hipError_t launch_sym256(const NsGroup* groups, int n, int mode, float ca, float cb, float cc,
+                         hipStream_t s) {
+  // per-tile work is the K loop: np for GRAM, mp for POLY
+  auto K = [&](const NsGroup* G) { return mode == GRAM ? G->np : G->mp; };
+  std::vector<const NsGroup*> order(n);
+  for (int i = 0; i < n; ++i) order[i] = groups + i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](const NsGroup* x, const NsGroup* y) { return K(x) > K(y); });
+  for (int c0 = 0; c0 < n; c0 += kMaxLaunchGroups) {
+    Sym256Launch a{};
+    a.a = ca;
+    a.b = cb;
+    a.c = cc;
+    int total = 0, left = 0;
+    a.split.n = std::min(kMaxLaunchGroups, n - c0);
+    for (int k = 0; k < a.split.n; ++k) {
+      const NsGroup& G = *order[c0 + k];
+      Sym256Args& g = a.g[k];
+      g.in = static_cast<const uint16_t*>(mode == GRAM ? G.x_in : G.a);
+      g.out = static_cast<uint16_t*>(mode == GRAM ? G.a : G.b);
+      g.scales = (mode == GRAM && G.first) ? G.scales : nullptr;
+      g.in_bs = mode == GRAM ? (long long)G.mp * G.np : (long long)G.mp * G.mp;
+      g.ld_in = K(&G);
+      g.K = K(&G);
+      g.mp = G.mp;
+      g.tiles = (G.mp + TS - 1) / TS;
+      g.tiles_per_mat = g.tiles * (g.tiles + 1) / 2;
+      const int tiles = g.tiles_per_mat * G.batch;
+      a.split.q[k] = tiles / 8;
+      a.split.r[k] = tiles % 8;
+      a.split.off[k] = left % 8;
+      left += tiles % 8;
+      total += tiles;
+    }
+    if (mode == GRAM)
+      hipLaunchKernelGGL(ns_sym256_bf16<GRAM>, dim3(total), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(ns_sym256_bf16<POLY>, dim3(total), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
-hipError_t launch_gram256_bf16(const NsGroup& G, hipStream_t s) {
-  Sym256Args a = sym256_args(G);
-  a.in = static_cast<const uint16_t*>(G.x_in);
-  a.out = static_cast<uint16_t*>(G.a);
-  a.in_bs = (long long)G.mp * G.np;
-  a.ld_in = G.np;
-  a.K = G.np;
-  a.scales = G.first ? G.scales : nullptr;
-  hipLaunchKernelGGL(ns_sym256_bf16<GRAM>, dim3(a.total_tiles), dim3(256), 0, s, a);
-  return hipGetLastError();
+}  // namespace
+
+hipError_t launch_gram256_bf16(const NsGroup* groups, int n, hipStream_t s) {
+  return launch_sym256(groups, n, GRAM, 0.f, 0.f, 0.f, s);
 }
 
-hipError_t launch_poly256_bf16(const NsGroup& G, float ca, float cb, float cc, hipStream_t s) {
-  Sym256Args a = sym256_args(G);
-  a.in = static_cast<const uint16_t*>(G.a);
-  a.out = static_cast<uint16_t*>(G.b);
-  a.in_bs = (long long)G.mp * G.mp;
-  a.ld_in = G.mp;
-  a.K = G.mp;
-  a.a = ca;
-  a.b = cb;
-  a.c = cc;
-  hipLaunchKernelGGL(ns_sym256_bf16<POLY>, dim3(a.total_tiles), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float ca, float cb, float cc,
+                               hipStream_t s) {
+  return launch_sym256(groups, n, POLY, ca, cb, cc, s);
 }
 
 }  // namespace muon

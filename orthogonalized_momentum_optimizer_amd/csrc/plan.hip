@@ -78,14 +78,6 @@ struct muon_plan {
   int ev_used = 0;             // pairs recorded by the pending call
   double prof_ms[MUON_KERNEL_KINDS] = {};
   int64_t prof_launches[MUON_KERNEL_KINDS] = {};
-  // concurrent shape groups: group -> lane (internal stream); lanes are created on the first
-  // call that needs them, on the device current then
-  std::vector<int> group_lane;
-  int nlanes = 0;
-  int lane_dev = -1;
-  std::vector<hipStream_t> lanes;
-  hipEvent_t fork = nullptr;
-  std::vector<hipEvent_t> joins;
 };
 
 namespace {
@@ -176,186 +168,116 @@ struct Launcher {
 
 // ---- the step ----------------------------------------------------------------------------
 
-void release_lanes(muon_plan* p) {
-  for (hipStream_t s : p->lanes) (void)hipStreamDestroy(s);
-  for (hipEvent_t e : p->joins) (void)hipEventDestroy(e);
-  if (p->fork) (void)hipEventDestroy(p->fork);
-  p->lanes.clear();
-  p->joins.clear();
-  p->fork = nullptr;
-  p->lane_dev = -1;
-}
-
-// Internal streams for concurrent shape groups, created once per device.
-int ensure_lanes(muon_plan* p) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
-  if (!p->lanes.empty() && p->lane_dev == dev) return MUON_OK;
-  release_lanes(p);
-  p->lane_dev = dev;
-  if (hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess) {
-    p->fork = nullptr;
-    release_lanes(p);
-    return fail(MUON_ERR_HIP, "creating the plan's fork event failed");
-  }
-  for (int i = 0; i < p->nlanes; ++i) {
-    hipStream_t s = nullptr;
-    hipEvent_t e = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
-      release_lanes(p);
-      return fail(MUON_ERR_HIP, "creating the plan's internal stream %d failed", i);
-    }
-    p->lanes.push_back(s);
-    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
-      release_lanes(p);
-      return fail(MUON_ERR_HIP, "creating the plan's join event %d failed", i);
-    }
-    p->joins.push_back(e);
-  }
-  return MUON_OK;
-}
-
-// One shape group's whole chain: momentum, norm, the Newton-Schulz rounds, the update.
+// The step, group by group: momentum, norm, the Newton-Schulz rounds and the update of one
+// shape group before the next group starts. Consecutive launches of one group then find their
+// operands (X, A, B', at most ~60 MB for a group of GPT-2 matrices) still in the MI355X's
+// 256 MB Infinity Cache; running each phase over all groups before the next phase was
+// measured 3-6% slower per kernel.
 // grads: per matrix input (grad or NS input); moms: momentum (nullable array = no momentum
 // phase); params: W (nullable array = no update); outs: O destination (nullable entries);
 // out_param_dtype: O is written in the param dtype (else fp32).
-int enqueue_group(muon_plan* p, size_t gi, const void* const* grads, float* const* moms,
-                  void* const* params, void* const* outs, bool out_param_dtype,
-                  const muon_config* cfg, char* base, hipStream_t stream) {
-  Launcher L{p, stream};
-  const bool f32 = p->prec == MUON_NS_F32_DEBUG;
-  const size_t esz = f32 ? 4 : 2;
-  const Group& G = p->groups[gi];
-  char* x0 = base + G.off_x0;
-  char* x1 = base + G.off_x1;
-  float* part = reinterpret_cast<float*>(base + G.off_part);
-  float* scales = reinterpret_cast<float*>(base + G.off_scales);
-  const size_t xslot = (size_t)G.mp * G.np * esz;
-
-  // phase 1: momentum, norm partials, X0
-  for (int si : G.sets) {
-    const LaunchSet& S = p->sets[si];
-    for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
-      ElemLaunch E{};
-      E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
-      for (int q = 0; q < E.count; ++q) {
-        const int m = S.mats[q0 + q];
-        E.in[q] = grads[m];
-        E.mom[q] = moms ? moms[m] : nullptr;
-      }
-      E.rows = S.rows;
-      E.cols = S.cols;
-      E.tall = S.rows > S.cols;
-      E.mp = G.mp;
-      E.np = G.np;
-      E.vec = (S.cols % 4) == 0;
-      const int slot = S.slot0 + (int)q0;
-      E.x = x0 + (size_t)slot * xslot;
-      E.partials = part + (size_t)slot * G.tiles64;
-      E.beta = cfg->beta;
-      E.nesterov = cfg->nesterov ? 1 : 0;
-      L.run(MUON_KERNEL_MOMENTUM, "momentum",
-            [&] { return launch_momentum(E, S.gdt == MUON_DT_F32, f32, stream); });
-    }
-  }
-  L.run(MUON_KERNEL_NORM, "norm",
-        [&] { return launch_norm(part, G.tiles64, scales, G.count, cfg->eps, stream); });
-
-  // phase 2: Newton-Schulz rounds, ping-pong between x0 and x1
-  NsGroup N{};
-  N.a = base + G.off_a;
-  N.b = base + G.off_b;
-  N.scales = scales;
-  N.batch = G.count;
-  N.mp = G.mp;
-  N.np = G.np;
-  char* xin = x0;
-  char* xout = x1;
-  for (int r = 0; r < cfg->ns_steps; ++r) {
-    N.x_in = xin;
-    N.x_out = xout;
-    N.first = r == 0;
-    const float* abc = cfg->schedule ? cfg->schedule + 3 * r : &cfg->a;
-    const float ca = abc[0], cb = abc[1], cc = abc[2];
-    L.run(MUON_KERNEL_GRAM, "gram",
-          [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(N, stream); });
-    L.run(MUON_KERNEL_POLY, "poly", [&] {
-      return f32 ? launch_poly_f32(N, cb, cc, stream) : launch_poly_bf16(N, ca, cb, cc, stream);
-    });
-    L.run(MUON_KERNEL_APPLY, "apply", [&] {
-      return f32 ? launch_apply_f32(N, ca, stream) : launch_apply_bf16(N, stream);
-    });
-    std::swap(xin, xout);
-  }
-
-  // phase 3: parameter update (and O output)
-  for (int si : G.sets) {
-    const LaunchSet& S = p->sets[si];
-    for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
-      ElemLaunch E{};
-      E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
-      for (int q = 0; q < E.count; ++q) {
-        const int m = S.mats[q0 + q];
-        E.param[q] = params ? params[m] : nullptr;
-        E.out[q] = outs ? outs[m] : nullptr;
-      }
-      E.rows = S.rows;
-      E.cols = S.cols;
-      E.tall = S.rows > S.cols;
-      E.mp = G.mp;
-      E.np = G.np;
-      E.vec = (S.cols % 4) == 0;
-      const int slot = S.slot0 + (int)q0;
-      E.x = xin + (size_t)slot * xslot;
-      E.scales = scales + 4 * (size_t)slot;
-      E.apply_scale = cfg->ns_steps == 0;
-      E.lr = cfg->lr;
-      const int out_dt = out_param_dtype ? (S.pdt == MUON_DT_F32) : 1;
-      L.run(MUON_KERNEL_UPDATE, "update",
-            [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
-    }
-  }
-  return L.status;
-}
-
-// The whole call. Shape groups share nothing (matrices, workspace regions), so with more
-// than one group each group's chain runs on one of the plan's internal streams, forked from
-// and joined back into the caller's stream: a group's launches fill the CUs that another
-// group's launch leaves idle (the tail of a launch whose tiles do not divide evenly over the
-// CUs). While profiling, every launch runs in order on the caller's stream, so each
-// kernel's time is its own.
 int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* const* params,
             void* const* outs, bool out_param_dtype, const muon_config* cfg, void* ws,
             hipStream_t stream) {
   prof_collect(p);
+  Launcher L{p, stream};
+  const bool f32 = p->prec == MUON_NS_F32_DEBUG;
+  const size_t esz = f32 ? 4 : 2;
   char* base = static_cast<char*>(ws);
-  const bool concurrent = p->nlanes > 1 && !p->prof;
-  if (!concurrent) {
-    for (size_t gi = 0; gi < p->groups.size(); ++gi)
-      if (int st = enqueue_group(p, gi, grads, moms, params, outs, out_param_dtype, cfg, base,
-                                 stream))
-        return st;
-    return MUON_OK;
+
+  for (size_t gi = 0; gi < p->groups.size(); ++gi) {
+    const Group& G = p->groups[gi];
+    char* x0 = base + G.off_x0;
+    float* part = reinterpret_cast<float*>(base + G.off_part);
+    float* scales = reinterpret_cast<float*>(base + G.off_scales);
+    const size_t xslot = (size_t)G.mp * G.np * esz;
+
+    // phase 1: momentum, norm partials, X0
+    for (int si : G.sets) {
+      const LaunchSet& S = p->sets[si];
+      for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
+        ElemLaunch E{};
+        E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
+        for (int q = 0; q < E.count; ++q) {
+          const int m = S.mats[q0 + q];
+          E.in[q] = grads[m];
+          E.mom[q] = moms ? moms[m] : nullptr;
+        }
+        E.rows = S.rows;
+        E.cols = S.cols;
+        E.tall = S.rows > S.cols;
+        E.mp = G.mp;
+        E.np = G.np;
+        E.vec = (S.cols % 4) == 0;
+        const int slot = S.slot0 + (int)q0;
+        E.x = x0 + (size_t)slot * xslot;
+        E.partials = part + (size_t)slot * G.tiles64;
+        E.beta = cfg->beta;
+        E.nesterov = cfg->nesterov ? 1 : 0;
+        L.run(MUON_KERNEL_MOMENTUM, "momentum",
+              [&] { return launch_momentum(E, S.gdt == MUON_DT_F32, f32, stream); });
+      }
+    }
+    L.run(MUON_KERNEL_NORM, "norm",
+          [&] { return launch_norm(part, G.tiles64, scales, G.count, cfg->eps, stream); });
+
+    // phase 2: Newton-Schulz rounds, ping-pong between x0 and x1
+    NsGroup N{};
+    N.x_in = x0;
+    N.x_out = base + G.off_x1;
+    N.a = base + G.off_a;
+    N.b = base + G.off_b;
+    N.scales = scales;
+    N.batch = G.count;
+    N.mp = G.mp;
+    N.np = G.np;
+    for (int r = 0; r < cfg->ns_steps; ++r) {
+      N.first = r == 0;
+      const float* abc = cfg->schedule ? cfg->schedule + 3 * r : &cfg->a;
+      const float ca = abc[0], cb = abc[1], cc = abc[2];
+      L.run(MUON_KERNEL_GRAM, "gram",
+            [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(&N, 1, stream); });
+      L.run(MUON_KERNEL_POLY, "poly", [&] {
+        return f32 ? launch_poly_f32(N, cb, cc, stream)
+                   : launch_poly_bf16(&N, 1, ca, cb, cc, stream);
+      });
+      L.run(MUON_KERNEL_APPLY, "apply", [&] {
+        return f32 ? launch_apply_f32(N, ca, stream) : launch_apply_bf16(&N, 1, stream);
+      });
+      std::swap(N.x_in, N.x_out);
+    }
+
+    // phase 3: parameter update (and O output)
+    char* xres = static_cast<char*>(N.x_in);
+    for (int si : G.sets) {
+      const LaunchSet& S = p->sets[si];
+      for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
+        ElemLaunch E{};
+        E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
+        for (int q = 0; q < E.count; ++q) {
+          const int m = S.mats[q0 + q];
+          E.param[q] = params ? params[m] : nullptr;
+          E.out[q] = outs ? outs[m] : nullptr;
+        }
+        E.rows = S.rows;
+        E.cols = S.cols;
+        E.tall = S.rows > S.cols;
+        E.mp = G.mp;
+        E.np = G.np;
+        E.vec = (S.cols % 4) == 0;
+        const int slot = S.slot0 + (int)q0;
+        E.x = xres + (size_t)slot * xslot;
+        E.scales = scales + 4 * (size_t)slot;
+        E.apply_scale = cfg->ns_steps == 0;
+        E.lr = cfg->lr;
+        const int out_dt = out_param_dtype ? (S.pdt == MUON_DT_F32) : 1;
+        L.run(MUON_KERNEL_UPDATE, "update",
+              [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
+      }
+    }
+    if (L.status != MUON_OK) return L.status;
   }
-  if (int st = ensure_lanes(p)) return st;
-  if (hipEventRecord(p->fork, stream) != hipSuccess)
-    return fail(MUON_ERR_HIP, "recording the fork event on the call's stream failed");
-  int status = MUON_OK;
-  for (int i = 0; i < p->nlanes && status == MUON_OK; ++i)
-    if (hipStreamWaitEvent(p->lanes[i], p->fork, 0) != hipSuccess)
-      status = fail(MUON_ERR_HIP, "internal stream %d cannot wait for the call's stream", i);
-  for (size_t gi = 0; gi < p->groups.size() && status == MUON_OK; ++gi)
-    status = enqueue_group(p, gi, grads, moms, params, outs, out_param_dtype, cfg, base,
-                           p->lanes[p->group_lane[gi]]);
-  // join every lane even after a failure, so the caller's stream never runs ahead of work
-  // that was enqueued
-  for (int i = 0; i < p->nlanes; ++i) {
-    const bool ok = hipEventRecord(p->joins[i], p->lanes[i]) == hipSuccess &&
-                    hipStreamWaitEvent(stream, p->joins[i], 0) == hipSuccess;
-    if (!ok && status == MUON_OK)
-      status = fail(MUON_ERR_HIP, "joining internal stream %d into the call's stream failed", i);
-  }
-  return status;
+  return L.status;
 }
 
 }  // namespace
@@ -463,27 +385,6 @@ int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
   }
   p->ws_bytes = off;
 
-  // Lanes for concurrent groups: longest-processing-time first over estimated
-  // Newton-Schulz flops (4 m^2 n + 2 m^3 per matrix), at most kMaxLanes.
-  constexpr int kMaxLanes = 4;
-  const int ng = (int)p->groups.size();
-  p->nlanes = std::min(ng, kMaxLanes);
-  p->group_lane.assign(ng, 0);
-  if (p->nlanes > 1) {
-    std::vector<int> order(ng);
-    std::vector<double> cost(ng), load(p->nlanes, 0.0);
-    for (int g = 0; g < ng; ++g) {
-      const double m = p->groups[g].mp, w = p->groups[g].np;
-      cost[g] = p->groups[g].count * (4.0 * m * m * w + 2.0 * m * m * m);
-      order[g] = g;
-    }
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost[a] > cost[b]; });
-    for (int g : order) {
-      const int lane = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-      p->group_lane[g] = lane;
-      load[lane] += cost[g];
-    }
-  }
   *out = p;
   return MUON_OK;
 }
@@ -590,7 +491,6 @@ void muon_plan_destroy(muon_plan* plan) {
     prof_collect(plan);
     for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
   }
-  release_lanes(plan);
   delete plan;
 }
 

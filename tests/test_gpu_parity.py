@@ -39,11 +39,11 @@ def test_ragged_shapes_fp32_params(precision):
 
 @pytest.mark.parametrize("precision", ["bf16"])
 def test_large_tile_products_ragged(precision):
-    """Shape groups with mp >= 512 use 256x256 tiles for the Gram and polynomial products:
-    mp = 640 leaves the last tile row half outside the matrix, 512 is exactly two tiles, and
-    the tall 1000x530 runs transposed (mp 640, np 1024)."""
+    """Shape groups with mp >= 1024 use 256x256 tiles for the Gram and polynomial products:
+    mp = 1152 leaves the last tile row half outside the matrix, 1024 is exactly four tiles,
+    and the tall 1400x1030 runs transposed (mp 1152, np 1408)."""
     _announce(f"256-tile products {precision}")
-    wl = si.custom([(640, 640), (600, 1000), (1000, 530), (512, 512), (512, 1536)],
+    wl = si.custom([(1100, 1100), (1030, 1400), (1400, 1030), (1024, 1024), (1024, 1536)],
                    cfg_id=111, steps=2)
     gpu = run_gpu(wl, 2, precision)
     compare(wl, gpu, 2, precision)
