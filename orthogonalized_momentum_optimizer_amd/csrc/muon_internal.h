@@ -53,10 +53,11 @@ struct NsGroup {
 };
 // bf16 storage, bf16 matrix cores with fp32 accumulation. The bf16 round folds a I into B:
 // poly writes B' = aI + bA + cAA and apply forms s1 B' X. Each launcher takes one or more
-// shape groups of a round (the step passes one group at a time): groups with use_sym256
-// (mp >= 1024) share 256x256-tile launches (one per 8 groups, ns_sym256_bf16.hip; apply
-// always, ns_apply_bf16.hip), tiles ordered longest first on every XCD; smaller groups use
-// 128x128 tiles, one launch each (ns_gemm_bf16.hip).
+// shape groups of a round (the step passes one group at a time). Gram and poly: groups with
+// use_sym256 (mp >= 1024) share 256x256-tile launches (one per 8 groups, tiles ordered
+// longest first on every XCD; ns_sym256_bf16.hip), smaller groups use 128x128 tiles, one
+// launch each (ns_gemm_bf16.hip). Apply: 256x256 tiles, one launch per group
+// (ns_apply_bf16.hip).
 bool use_sym256(const NsGroup& g);
 hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s);   // A = s2 X X^T
 hipError_t launch_poly_bf16(const NsGroup* groups, int n, float a, float b, float c,

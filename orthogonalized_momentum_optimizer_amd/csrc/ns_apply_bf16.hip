@@ -23,9 +23,6 @@
 // With the MFMA operands passed as (right, left), accumulator block (i, j) holds the
 // transposed product: element r of lane l is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4],
 // so each register quad is 4 consecutive columns of one row: one 8-byte store.
-#include <algorithm>
-#include <vector>
-
 #include "mfma_common.h"
 
 namespace muon {
@@ -44,12 +41,7 @@ struct ApplyArgs {      // one shape group
   uint16_t* out;       // X', batch x mp x np
   const float* scales; // per matrix {s1, s2, nu, 0}, or null (scale 1)
   int mp, np;
-  int tiles_m, tiles_n;
-};
-
-struct ApplyLaunch {   // the shape groups of one launch, longest tiles (largest mp) first
-  TileSplit split;
-  ApplyArgs g[kMaxLaunchGroups];
+  int tiles_m, tiles_n, total_tiles;
 };
 
 // Fragments of one 16-wide K slice: 8 transposed half-fragments of the right operand and 4
@@ -74,7 +66,7 @@ __device__ __forceinline__ void lds_op(uint32_t va, uint32_t vb, Frags& f) {
   }
 }
 
-__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyLaunch A) {
+__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB
 
   const int t = threadIdx.x;
@@ -83,8 +75,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyLaunch A) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
-  int L;
-  const ApplyArgs g = A.g[split_block(blockIdx.x, A.split, L)];
+  const int L = xcd_remap(blockIdx.x, g.total_tiles);
   const int per_mat = g.tiles_m * g.tiles_n;
   const int bidx = L / per_mat;
   const int tt = L - bidx * per_mat;
@@ -286,34 +277,22 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyLaunch A) {
 
 }  // namespace
 
+// One launch per group: a grid over several groups (each XCD taking its share of each) was
+// measured no faster for this kernel, whose tiles all cost the same for a given mp.
 hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
-  std::vector<const NsGroup*> order(n);
-  for (int i = 0; i < n; ++i) order[i] = groups + i;
-  std::stable_sort(order.begin(), order.end(),
-                   [](const NsGroup* x, const NsGroup* y) { return x->mp > y->mp; });
-  for (int c0 = 0; c0 < n; c0 += kMaxLaunchGroups) {
-    ApplyLaunch a{};
-    int total = 0, left = 0;
-    a.split.n = std::min(kMaxLaunchGroups, n - c0);
-    for (int k = 0; k < a.split.n; ++k) {
-      const NsGroup& G = *order[c0 + k];
-      ApplyArgs& g = a.g[k];
-      g.b = static_cast<const uint16_t*>(G.b);
-      g.x = static_cast<const uint16_t*>(G.x_in);
-      g.out = static_cast<uint16_t*>(G.x_out);
-      g.scales = G.first ? G.scales : nullptr;
-      g.mp = G.mp;
-      g.np = G.np;
-      g.tiles_m = (G.mp + TM - 1) / TM;
-      g.tiles_n = (G.np + TN - 1) / TN;
-      const int tiles = g.tiles_m * g.tiles_n * G.batch;
-      a.split.q[k] = tiles / 8;
-      a.split.r[k] = tiles % 8;
-      a.split.off[k] = left % 8;
-      left += tiles % 8;
-      total += tiles;
-    }
-    hipLaunchKernelGGL(ns_apply_bf16, dim3(total), dim3(256), 0, s, a);
+  for (int k = 0; k < n; ++k) {
+    const NsGroup& G = groups[k];
+    ApplyArgs a{};
+    a.b = static_cast<const uint16_t*>(G.b);
+    a.x = static_cast<const uint16_t*>(G.x_in);
+    a.out = static_cast<uint16_t*>(G.x_out);
+    a.scales = G.first ? G.scales : nullptr;
+    a.mp = G.mp;
+    a.np = G.np;
+    a.tiles_m = (G.mp + TM - 1) / TM;
+    a.tiles_n = (G.np + TN - 1) / TN;
+    a.total_tiles = a.tiles_m * a.tiles_n * G.batch;
+    hipLaunchKernelGGL(ns_apply_bf16, dim3(a.total_tiles), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;
