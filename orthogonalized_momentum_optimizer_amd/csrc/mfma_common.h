@@ -177,6 +177,21 @@ __device__ __forceinline__ u32x4 ds_read_b128_at(uint32_t addr) {
   return r;
 }
 
+// 8-byte LDS write issued as inline assembly: while direct-to-LDS loads are outstanding,
+// the compiler would otherwise wait for all of them (vmcnt 0) before any LDS access it
+// cannot prove disjoint from their destinations.
+__device__ __forceinline__ void ds_write_b64_at(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// A float at a wave-uniform global address, through the scalar cache (a scalar load: it
+// does not count against vmcnt, so reading it never waits for outstanding vector loads).
+__device__ __forceinline__ float scalar_load_f32(const float* p) {
+  float v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // Calls f(std::integral_constant<int, i>) for i = 0..N-1, unrolled at compile time.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

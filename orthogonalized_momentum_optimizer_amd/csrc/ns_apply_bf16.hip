@@ -23,6 +23,8 @@
 // With the MFMA operands passed as (right, left), accumulator block (i, j) holds the
 // transposed product: element r of lane l is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4],
 // so each register quad is 4 consecutive columns of one row: one 8-byte store.
+#include <algorithm>
+
 #include "mfma_common.h"
 
 namespace muon {
@@ -66,8 +68,11 @@ __device__ __forceinline__ void lds_op(uint32_t va, uint32_t vb, Frags& f) {
   }
 }
 
+// Output staging of the epilogue: 64 rows x 256 columns of bf16 (32 KB) beside the ring.
+constexpr int kUnitsOut = 64 * TN / 8;
+
 __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
-  __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB
+  __shared__ u32x4 smem[NSTAGE * kUnitsStage + kUnitsOut];  // 128 KB ring + 32 KB staging
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -75,56 +80,62 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
-  const int L = xcd_remap(blockIdx.x, g.total_tiles);
+  // ---- persistent tile loop ----
+  // Block k of XCD x (blockIdx % 8 = x) takes tiles lo + k, lo + k + nb, ... of the XCD's
+  // contiguous range [lo, hi) of the group's tiles (nb = the XCD's block count), so the CUs
+  // of one XCD work on neighbouring tiles of the same matrices at the same time.
+  const int x = blockIdx.x & 7, k0 = blockIdx.x >> 3;
+  const int T = g.total_tiles, G = gridDim.x;
+  const int lo = xcd_remap(x, T);  // first tile of XCD x
+  const int nt = T / 8 + (x < (T & 7) ? 1 : 0);
+  const int nb = G / 8 + (x < (G & 7) ? 1 : 0);
   const int per_mat = g.tiles_m * g.tiles_n;
-  const int bidx = L / per_mat;
-  const int tt = L - bidx * per_mat;
-  const int I = tt / g.tiles_n, J = tt - (tt / g.tiles_n) * g.tiles_n;
-
   const size_t mm = (size_t)g.mp * g.mp, mn = (size_t)g.mp * g.np;
-  const char* lhs = reinterpret_cast<const char*>(g.b + bidx * mm);
-  const char* rhs = reinterpret_cast<const char*>(g.x + bidx * mn);
   const size_t rhs_stage_bytes = (size_t)2 * TK * g.np;
-  const int row0 = I * TM, col0 = J * TN;
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   const int KT = g.mp / TK;
 
-  // ---- direct-to-LDS loads: 8 per wave per stage, one instruction each ----
-  // Loads 0-3 fetch 16 left-operand rows each (4 lanes x 16 bytes per row), loads 4-7 two
-  // right-operand K-rows each (32 lanes x 16 bytes per row); lane l lands at 16 l of a 1 KB
-  // LDS block, so the swizzle is applied by choosing the global chunk a lane fetches. The
-  // global address is a wave-uniform base (the operand's stage origin, in scalar registers)
-  // plus the lane's 32-bit byte offset below, fixed for the whole loop.
-  uint32_t doff[8];
+  struct Tile {
+    int bidx, row0, col0;
+    const char* lhs;
+    const char* rhs;
+    uint32_t doff[8];
+  };
+  // Direct-to-LDS loads, 8 per wave per stage, one instruction each: loads 0-3 fetch 16
+  // left-operand rows each (4 lanes x 16 bytes per row), loads 4-7 two right-operand K-rows
+  // each (32 lanes x 16 bytes per row); lane l lands at 16 l of a 1 KB LDS block, so the
+  // swizzle is applied by choosing the global chunk a lane fetches. The global address is a
+  // wave-uniform base (the operand's stage origin, in scalar registers) plus the lane's
+  // 32-bit byte offset, fixed for the tile.
+  auto setup = [&](int L, Tile& c) {
+    c.bidx = L / per_mat;
+    const int tt = L - c.bidx * per_mat;
+    const int I = tt / g.tiles_n, J = tt - (tt / g.tiles_n) * g.tiles_n;
+    c.row0 = I * TM;
+    c.col0 = J * TN;
+    c.lhs = reinterpret_cast<const char*>(g.b + c.bidx * mm);
+    c.rhs = reinterpret_cast<const char*>(g.x + c.bidx * mn);
 #pragma unroll
-  for (int op = 0; op < 4; ++op) {
-    const int row = 16 * (4 * wave + op) + (lane >> 2);
-    const int c = (lane & 3) ^ kswz(row);
-    const uint32_t grow = min(row0 + row, g.mp - 1);
-    doff[op] = 2u * (grow * (uint32_t)g.mp + 8u * c);
-  }
+    for (int op = 0; op < 4; ++op) {
+      const int row = 16 * (4 * wave + op) + (lane >> 2);
+      const int ch = (lane & 3) ^ kswz(row);
+      const uint32_t grow = min(c.row0 + row, g.mp - 1);
+      c.doff[op] = 2u * (grow * (uint32_t)g.mp + 8u * ch);
+    }
 #pragma unroll
-  for (int op = 0; op < 4; ++op) {
-    const int k = 2 * (4 * wave + op) + (lane >> 5);
-    const int c = (lane & 31) ^ (2 * (k & 3));
-    const uint32_t gcol = min(col0 + 8 * c, g.np - 8);
-    doff[4 + op] = 2u * ((uint32_t)k * (uint32_t)g.np + gcol);
-  }
-  auto dma_op = [&](int kt, int op) {
+    for (int op = 0; op < 4; ++op) {
+      const int kk = 2 * (4 * wave + op) + (lane >> 5);
+      const int ch = (lane & 31) ^ (2 * (kk & 3));
+      const uint32_t gcol = min(c.col0 + 8 * ch, g.np - 8);
+      c.doff[4 + op] = 2u * ((uint32_t)kk * (uint32_t)g.np + gcol);
+    }
+  };
+  auto dma_op = [&](const Tile& c, int kt, int op) {
     u32x4* st = smem + (kt & (NSTAGE - 1)) * kUnitsStage;
     if (op < 4)
-      __builtin_amdgcn_global_load_lds(lhs + (size_t)kt * (2 * TK) + doff[op],
+      __builtin_amdgcn_global_load_lds(c.lhs + (size_t)kt * (2 * TK) + c.doff[op],
                                        MUON_LDS_PTR(st + 64 * (4 * wave + op)), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(rhs + (size_t)kt * rhs_stage_bytes + doff[op],
+      __builtin_amdgcn_global_load_lds(c.rhs + (size_t)kt * rhs_stage_bytes + c.doff[op],
                                        MUON_LDS_PTR(st + kUnitsA + 64 * (4 * wave + op - 4)),
                                        16, 0, 0);
   };
@@ -163,12 +174,15 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, f.av[i]);
   };
+  f32x16 acc[4][4];
   auto mfma = [&](int m, const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
     const int i = m >> 2, j = m & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
   };
-  // Waits for this wave's loads of the next stage (`later` stages issued after it), then the
-  // block barrier: that stage is complete for every wave.
+  // Waits for this wave's loads of the next stage, then the block barrier: that stage is
+  // complete for every wave. `later` counts the loads issued after it; any vector-memory
+  // operation issued in between (the previous tile's output stores) only makes the wait
+  // longer, never too short: the counter completes in issue order.
   auto stage_ready = [&](int later) {
     if (later >= 3) vm_wait<3 * kLoadsPerStage>();
     else if (later == 2) vm_wait<2 * kLoadsPerStage>();
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
   };
 
-  // ---- software pipeline ----
+  // ---- software pipeline of one tile ----
   // Per stage, two batches of 16 MFMAs (one per K slice). While batch 0 runs, the 12 reads
   // of slice 1 are issued between its MFMAs; then (slice 1 in registers, so this wave is done
   // with the stage) the next stage's barrier; while batch 1 runs, the 8 direct loads of stage
@@ -187,10 +201,11 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   // the refills stop and before the last stage, so neither condition is a branch inside it.
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   Frags f0, f1;
+  Tile cur;
   auto iteration = [&](int kt, auto refill_t, auto more_t) {
     constexpr bool refill = decltype(refill_t)::value, more = decltype(more_t)::value;
-    const uint32_t cur = stage_base(kt);
-    const uint32_t va1 = cur + aoff1, vb = cur + boff;
+    const uint32_t cb = stage_base(kt);
+    const uint32_t va1 = cb + aoff1, vb = cb + boff;
     __builtin_amdgcn_sched_barrier(0);
     static_for<16>([&](auto M) {
       constexpr int m = decltype(M)::value;
@@ -211,71 +226,123 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
       constexpr int m = decltype(M)::value;
       mfma(m, a1, b1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (refill && m < 8) dma_op(kt + NSTAGE, m);
+      if constexpr (refill && m < 8) dma_op(cur, kt + NSTAGE, m);
       if constexpr (more && m >= 2 && m < 14) lds_op<0, m - 2>(va0n, vbn, f0);
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (more) ready(f0, a0, b0);
   };
 
-#pragma unroll
-  for (int st = 0; st < NSTAGE; ++st)
-#pragma unroll
-    for (int op = 0; op < 8; ++op) dma_op(st, op);  // KT >= 4: mp is a multiple of 128
-  stage_ready(NSTAGE - 1);
-  static_for<12>([&](auto OP) { lds_op<0, decltype(OP)::value>(lds0 + aoff0, lds0 + boff, f0); });
-  ready(f0, a0, b0);
+  // Epilogue staging: chunk i holds tile rows 32i..32i+31 and 128+32i..128+32i+31 (the
+  // rows of every wave's accumulator block row i), 512-byte rows with 16-byte chunk q of row
+  // r at q ^ (r & 15).
 
-  int kt = 0;
-  for (; kt < KT - NSTAGE; ++kt) iteration(kt, std::true_type{}, std::true_type{});
-  for (; kt < KT - 1; ++kt) iteration(kt, std::false_type{}, std::true_type{});
-  iteration(KT - 1, std::false_type{}, std::false_type{});
+  int L = lo + k0;
+  const int hi = lo + nt;
+  if (L < hi) {
+    setup(L, cur);
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st)
+#pragma unroll
+      for (int op = 0; op < 8; ++op) dma_op(cur, st, op);  // KT >= 4: mp is a multiple of 128
+  }
+  for (; L < hi; L += nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    stage_ready(NSTAGE - 1);
+    static_for<12>([&](auto OP) { lds_op<0, decltype(OP)::value>(lds0 + aoff0, lds0 + boff, f0); });
+    ready(f0, a0, b0);
 
-  // Epilogue: scale, round to bf16 and stage the 256x256 tile in LDS (128 KB, the whole
-  // operand ring), then store 16-byte chunks with 32 lanes per 512-byte row segment; stores
-  // straight from the accumulator layout touch 32 rows per instruction and were measured to
-  // take longer than the whole main loop. Chunk q (8 columns) of row r sits at
-  // q ^ (r & 15): 16 lanes reading 16 chunks of one row, or writing one chunk of 16
-  // consecutive rows, hit distinct 16-byte bank groups.
-  const float s = g.scales ? g.scales[4 * bidx] : 1.f;
-  __syncthreads();  // every wave is done with the operand stages
-  u32x2* st2 = reinterpret_cast<u32x2*>(smem);  // 8-byte units: row * 64 + 2 * chunk + half
-  // the scale is 1 after the first round: skip its 256 multiplies per lane there
-  auto stage_out = [&](auto scaled_t) {
-    constexpr bool scaled = decltype(scaled_t)::value;
+    int kt = 0;
+    for (; kt < KT - NSTAGE; ++kt) iteration(kt, std::true_type{}, std::true_type{});
+    for (; kt < KT - 1; ++kt) iteration(kt, std::false_type{}, std::true_type{});
+    iteration(KT - 1, std::false_type{}, std::false_type{});
+
+    // every wave is done with the ring: the next tile's first stages load while this tile's
+    // output drains through the staging area
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int bidx = cur.bidx, row0 = cur.row0, col0 = cur.col0;
+    if (L + nb < hi) {
+      setup(L + nb, cur);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wr * 128 + i * 32 + (lane & 31);
+      for (int st = 0; st < NSTAGE; ++st)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int op = 0; op < 8; ++op) dma_op(cur, st, op);
+    }
+
+    // the scale is 1 after the first round: skip its multiplies there. Every LDS access
+    // below is inline assembly and the scale a scalar load, so nothing here waits for the
+    // next tile's loads.
+    const float s = g.scales ? scalar_load_f32(g.scales + 4 * bidx) : 1.f;
+    uint16_t* out = g.out + bidx * mn;
+    const uint32_t stb = lds0 + 16u * (NSTAGE * kUnitsStage);  // staging base, bytes
+    auto stage_chunk = [&](int i, auto scaled_t) {
+      constexpr bool scaled = decltype(scaled_t)::value;
+      const int cr = wr * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = 64 * j + 32 * wc + 8 * q + 4 * (lane >> 5);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = scaled ? acc[i][j][4 * q + e] * s : acc[i][j][4 * q + e];
-          st2[row * 64 + 2 * ((col >> 3) ^ (row & 15)) + ((col >> 2) & 1)] =
-              u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+          ds_write_b64_at(stb + 512u * cr + 16u * ((col >> 3) ^ (cr & 15)) + 8u * ((col >> 2) & 1),
+                          u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
         }
+    };
+    // Barrier for the staging area only: waits for this wave's LDS accesses, not for its
+    // outstanding loads of the next tile (__syncthreads would wait for those too).
+    auto lds_barrier = [] {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    const int ch = t & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i > 0) lds_barrier();  // the previous chunk has been read out
+      if (g.scales) stage_chunk(i, std::true_type{});
+      else stage_chunk(i, std::false_type{});
+      lds_barrier();
+      u32x4 w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cr = (t >> 5) + 8 * k;
+        w[k] = ds_read_b128_at<0>(stb + 512u * cr + 16u * (ch ^ (cr & 15)));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
+                     "+v"(w[6]), "+v"(w[7]));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cr = (t >> 5) + 8 * k;
+        const int grow = row0 + 32 * i + (cr & 31) + 128 * (cr >> 5), gcol = col0 + 8 * ch;
+        if (grow < g.mp && gcol < g.np)
+          *reinterpret_cast<u32x4*>(out + (size_t)grow * g.np + gcol) = w[k];
       }
     }
-  };
-  if (g.scales) stage_out(std::true_type{});
-  else stage_out(std::false_type{});
-  __syncthreads();
-  uint16_t* out = g.out + bidx * mn;
-  const int ch = t & 31;
-#pragma unroll 8
-  for (int k = 0; k < 32; ++k) {
-    const int row = (t >> 5) + 8 * k;
-    const int grow = row0 + row, gcol = col0 + 8 * ch;
-    if (grow < g.mp && gcol < g.np)
-      *reinterpret_cast<u32x4*>(out + (size_t)grow * g.np + gcol) =
-          smem[row * 32 + (ch ^ (row & 15))];
   }
 }
 
 }  // namespace
+
+// Compute units of the current device (one persistent block each).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+    n = 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
 
 // One launch per group: a grid over several groups (each XCD taking its share of each) was
 // measured no faster for this kernel, whose tiles all cost the same for a given mp.
@@ -292,7 +359,8 @@ hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
     a.tiles_m = (G.mp + TM - 1) / TM;
     a.tiles_n = (G.np + TN - 1) / TN;
     a.total_tiles = a.tiles_m * a.tiles_n * G.batch;
-    hipLaunchKernelGGL(ns_apply_bf16, dim3(a.total_tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ns_apply_bf16, dim3(std::min(a.total_tiles, device_cus())), dim3(256), 0,
+                       s, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;
