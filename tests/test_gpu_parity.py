@@ -49,6 +49,16 @@ def test_large_tile_products_ragged(precision):
     compare(wl, gpu, 2, precision)
 
 
+def test_many_tiles_per_block_full_parity():
+    """300 matrices of 128x384 (mp 128, np 384): 600 apply tiles, more than the device has
+    compute units, so every persistent block walks several ragged tiles (each half outside
+    its matrix); every element of every matrix is compared."""
+    _announce("many tiles per block")
+    wl = si.custom([(128, 384)] * 150 + [(384, 128)] * 150, cfg_id=112, steps=2)
+    gpu = run_gpu(wl, 2, "bf16")
+    compare(wl, gpu, 2, "bf16")
+
+
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_gpt2_tiny_fp32_workload(precision):
     """64x256 fp32 matrix, one N(0,1) gradient reused for 3 steps."""
