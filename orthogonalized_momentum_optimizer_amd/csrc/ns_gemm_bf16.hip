@@ -120,63 +120,71 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
     const uint32_t grow = min((op < 2 ? I * BM : J * BN) + row, g.mp - 1);
     doff[op] = 2u * (grow * (uint32_t)g.ld_in + 8u * c);
   }
-  auto issue = [&](int kt) {
-    u32x4* st = smem + (kt & (STAGES - 1)) * kStage;
-    const char* base = srcb + (size_t)kt * (2 * BK);
+  // A diagonal tile (I == J) multiplies a row block by itself: it loads the block once and
+  // reads both operands from it (half the stage traffic of an off-diagonal tile).
+  auto run = [&](auto diag_t) {
+    constexpr bool kDiag = decltype(diag_t)::value;
+    constexpr int kLoads = kDiag ? 2 : kLoadsPerStage;  // direct loads per wave per stage
+    auto issue = [&](int kt) {
+      u32x4* st = smem + (kt & (STAGES - 1)) * kStage;
+      const char* base = srcb + (size_t)kt * (2 * BK);
 #pragma unroll
-    for (int op = 0; op < 4; ++op)
-      __builtin_amdgcn_global_load_lds(base + doff[op],
-                                       MUON_LDS_PTR(st + (op < 2 ? 0 : 512) +
-                                                    64 * (2 * wave + (op & 1))),
-                                       16, 0, 0);
-  };
+      for (int op = 0; op < kLoads; ++op)
+        __builtin_amdgcn_global_load_lds(base + doff[op],
+                                         MUON_LDS_PTR(st + (op < 2 ? 0 : 512) +
+                                                      64 * (2 * wave + (op & 1))),
+                                         16, 0, 0);
+    };
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
 
-  // One stage of the main loop. LATER: this wave's loads issued after stage kt's (two
-  // stages while refills run, then one, then none), so stage kt is in once at most LATER
-  // stages' loads are pending; REFILL: whether stage kt + 3 is loaded into the buffer that
-  // every wave finished with before this stage's barrier.
-  auto stage = [&](int kt, auto later_t, auto refill_t) {
-    constexpr int later = decltype(later_t)::value;
-    vm_wait<later * kLoadsPerStage>();
-    // every wave's loads of stage kt are visible, and every wave is done with stage kt - 1
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-    if constexpr (decltype(refill_t)::value) issue(kt + STAGES - 1);
+    // One stage of the main loop. LATER: this wave's loads issued after stage kt's (two
+    // stages while refills run, then one, then none), so stage kt is in once at most LATER
+    // stages' loads are pending; REFILL: whether stage kt + 3 is loaded into the buffer that
+    // every wave finished with before this stage's barrier.
+    auto stage = [&](int kt, auto later_t, auto refill_t) {
+      constexpr int later = decltype(later_t)::value;
+      vm_wait<later * kLoads>();
+      // every wave's loads of stage kt are visible, and every wave is done with stage kt - 1
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+      if constexpr (decltype(refill_t)::value) issue(kt + STAGES - 1);
 
-    const u32x4* A = smem + (kt % STAGES) * kStage;
-    const u32x4* B = A + 512;
-    if (MODE == POLY && (kt >> 2) == J && (kt & 3) == ((t & 15) >> 2)) {
+      const u32x4* A = smem + (kt % STAGES) * kStage;
+      const u32x4* B = kDiag ? A : A + 512;
+      if (MODE == POLY && (kt >> 2) == J && (kt & 3) == ((t & 15) >> 2)) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int row = (t >> 4) + 16 * k;
-        epre[k] = A[row * 4 + ((t & 3) ^ kswz(row))];
+        for (int k = 0; k < 8; ++k) {
+          const int row = (t >> 4) + 16 * k;
+          epre[k] = A[row * 4 + ((t & 3) ^ kswz(row))];
+        }
       }
-    }
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      bf16x8 af[2], bfr[2];
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int c = 2 * ks + (lane >> 5);
+        bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = frag_k(A, wr * 64 + i * 32 + (lane & 31), c);
+        for (int i = 0; i < 2; ++i) af[i] = frag_k(A, wr * 64 + i * 32 + (lane & 31), c);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = frag_k(B, wc * 64 + j * 32 + (lane & 31), c);
+        for (int j = 0; j < 2; ++j) bfr[j] = frag_k(B, wc * 64 + j * 32 + (lane & 31), c);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int kt = 0;
+    for (; kt < KT - (STAGES - 1); ++kt) stage(kt, I2{}, std::true_type{});
+    stage(kt++, I2{}, std::false_type{});
+    stage(kt++, I1{}, std::false_type{});
+    stage(kt, I0{}, std::false_type{});
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  int kt = 0;
-  for (; kt < KT - (STAGES - 1); ++kt) stage(kt, I2{}, std::true_type{});
-  stage(kt++, I2{}, std::false_type{});
-  stage(kt++, I1{}, std::false_type{});
-  stage(kt, I0{}, std::false_type{});
+  if (I == J) run(std::true_type{});
+  else run(std::false_type{});
   // all waves are done reading the operand stages before the epilogue reuses them
   __syncthreads();
 
