@@ -14,9 +14,12 @@ Sources (the pages are cited by title and section):
   "Muon优化器的能效突破" (Muon = momentum orthogonalised by Newton-Schulz).
 * [P4] the RecursiveFromBest record analysis (lqnn.cn/news/184262), section 3.2 "NorMuon
   中的退火行 RMS 缩放 Langevin/SGLD 探索噪声", which names Frobenius normalisation as the
-  step in front of the quintic maps of the Muon family.
+  step in front of the quintic maps of the Muon family; and section 3.3 "bigram 与
+  value-embedding 银行上的 C-Optim / 谨慎 Adam" (cautious Adam for the embedding-like
+  parameters, oracle/cautious_adam.py).
 
-Readings where the pages are silent are listed in muon.py's header.
+Readings where the pages are silent are listed in the headers of muon.py and
+cautious_adam.py.
 """
 from .muon import (  # noqa: F401
     DEFAULT_ABC,
@@ -26,4 +29,11 @@ from .muon import (  # noqa: F401
     orthogonalize,
     muon_step,
     muon_run,
+)
+from .cautious_adam import (  # noqa: F401
+    adam_moments,
+    adam_direction,
+    cautious_decay,
+    cautious_adam_step,
+    cautious_adam_run,
 )

@@ -139,3 +139,80 @@ def sample_indices(wl: Workload) -> List[int]:
         for j in sorted({idx[0], idx[len(idx) // 2], idx[-1]}):
             out.append(j)
     return sorted(out)
+
+
+# ---- non-matrix parameter sets (the Adam half of the optimizer table) ---------------------
+#
+# The record analysed at lqnn.cn (section 3.3) trains the embedding-like parameters with a
+# cautious Adam: the token embedding (tied with the LM head), value-embedding banks and a few
+# scalars, with decay multipliers 150 (embed / lm_head) and 0 (scalars). The pages give
+# neither the vocabulary nor the number of banks; the sets below use GPT-2's vocabulary of
+# 50257 tokens, width 768 and three value-embedding banks, which the pages' 124M model has
+# the width of. Value embeddings take the base decay (multiplier 1), since the page's table
+# names none for them. Draws use kinds 2 (parameters) and 3 (gradients).
+
+KIND_ADAM_PARAM = 2
+KIND_ADAM_GRAD = 3
+
+
+@dataclass(frozen=True)
+class AdamSet:
+    name: str
+    cfg_id: int
+    tensors: Tuple[Tuple[str, Tuple[int, ...], float], ...]   # (label, shape, wd_mul)
+    dtype: str                                                  # "bf16" or "f32" for p and g
+    steps: int
+    param_std: float = 0.02
+    grad_std: float = 1e-3
+
+    @property
+    def n(self) -> int:
+        return len(self.tensors)
+
+    def numel(self, i: int) -> int:
+        return int(np.prod(self.tensors[i][1], dtype=np.int64))
+
+    def elements(self) -> int:
+        return int(sum(self.numel(i) for i in range(self.n)))
+
+
+def _adam_sets() -> dict:
+    v, d = 50257, 768
+    s = {}
+    s["gpt2_124m_embed"] = AdamSet(
+        "gpt2_124m_embed", 20,
+        (("embed", (v, d), 150.0),) + tuple((f"value_embed{k}", (v, d), 1.0) for k in range(3))
+        + (("scalars", (64,), 0.0),),
+        "bf16", 10)
+    s["ragged_small"] = AdamSet(
+        "ragged_small", 21,
+        (("one", (1,), 1.0), ("odd", (37,), 150.0), ("rows", (5, 129), 1.0),
+         ("wide", (3, 1000), 0.0), ("even", (2048,), 150.0), ("vec_tail", (8191,), 1.0),
+         ("tile_tail", (3, 4097), 150.0), ("blocks", (70001,), 1.0)),
+        "f32", 4, param_std=0.5, grad_std=1.0)
+    return s
+
+
+ADAM_SETS = _adam_sets()
+
+
+def adam_param(s: AdamSet, index: int):
+    """Initial values of tensor ``index`` of an Adam set as a CPU torch tensor."""
+    x = rng(s.cfg_id, KIND_ADAM_PARAM, index, 0).normal(0.0, s.param_std,
+                                                        size=s.tensors[index][1])
+    return _to_stored(x, s.dtype)
+
+
+def adam_grad(s: AdamSet, index: int, step: int):
+    """Gradient of tensor ``index`` at step ``step`` (0-based) as a CPU torch tensor."""
+    x = rng(s.cfg_id, KIND_ADAM_GRAD, index, step).normal(0.0, s.grad_std,
+                                                          size=s.tensors[index][1])
+    return _to_stored(x, s.dtype)
+
+
+def adam_custom(shapes_wd, dtype: str = "f32", steps: int = 3, cfg_id: int = 200,
+                param_std: float = 0.5, grad_std: float = 1.0) -> AdamSet:
+    """An ad-hoc Adam set: ``shapes_wd`` is a list of (shape, wd_mul)."""
+    return AdamSet(f"adam_custom{cfg_id}", cfg_id,
+                   tuple((f"t{i}", tuple(sh), float(w)) for i, (sh, w) in enumerate(shapes_wd)),
+                   dtype, steps, param_std=param_std, grad_std=grad_std)
