@@ -12,6 +12,11 @@ two staged gradient batches used alternately). Prints one JSON line:
              by their summed duration, measured with the library's per-launch HIP events in
              a second timed pass, against the MI355X peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
+  next_rows  the cautious-Adam step for the non-matrix parameters of the same model (the
+             embedding-shaped set: 4 x 50257 x 768 bf16 + 64 scalars), timed on its own:
+             one launch per step, HBM bytes of the algorithm over the launch time
+
+    python bench.py --adam-only     times only the cautious-Adam step (for profiling it)
 """
 from __future__ import annotations
 
@@ -28,7 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import seeded_inputs as si  # noqa: E402
-from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config  # noqa: E402
+from orthogonalized_momentum_optimizer_amd import (  # noqa: E402
+    MuonPlan, cautious_adam_step, make_adam_config, make_config)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
@@ -54,6 +60,7 @@ def kind_work(wl, ns_steps=5):
 KERNEL_SOURCES = {   # kernel kind -> the source file that defines its bf16 kernel
     "apply": "ns_apply_bf16.hip", "gram": "ns_gemm_bf16.hip", "poly": "ns_gemm_bf16.hip",
     "momentum": "elementwise.hip", "update": "elementwise.hip", "norm": "elementwise.hip",
+    "cautious_adam": "cautious_adam.hip",
 }
 
 
@@ -113,6 +120,61 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{elapsed:.1f} s"}
 
 
+def adam_bytes_per_element(pdt="bf16", gdt="bf16"):
+    """Algorithmic HBM bytes of one cautious-Adam element: read p, g, m, v; write p, m, v."""
+    pe, ge = (2 if pdt == "bf16" else 4), (2 if gdt == "bf16" else 4)
+    return 2 * pe + ge + 16
+
+
+def bench_adam(steps, warmup, dev):
+    """Times the cautious-Adam step over the embedding-shaped set of the GPT-2-124M model on
+    HBM-resident tensors (parameters and two gradient batches drawn on the GPU from a seeded
+    generator; moments zero at the start)."""
+    aset = si.ADAM_SETS["gpt2_124m_embed"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(aset.cfg_id)
+    numels = [aset.numel(i) for i in range(aset.n)]
+    P = [(aset.param_std * torch.randn(n, generator=gen, device=dev)).to(torch.bfloat16)
+         for n in numels]
+    G = [[(aset.grad_std * torch.randn(n, generator=gen, device=dev)).to(torch.bfloat16)
+          for n in numels] for _ in range(2)]
+    M = [torch.zeros(n, dtype=torch.float32, device=dev) for n in numels]
+    V = [torch.zeros(n, dtype=torch.float32, device=dev) for n in numels]
+    muls = [w for _, _, w in aset.tensors]
+    lr, betas, eps, wd = 1e-3, (0.9, 0.95), 1e-8, 0.01
+    cfgs = [make_adam_config(lr, betas, eps, wd, t + 1) for t in range(warmup + steps)]
+    stream = torch.cuda.current_stream()
+    for t in range(warmup):
+        cautious_adam_step(P, G[t % 2], M, V, cfgs[t], muls)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for t in range(warmup, warmup + steps):
+        cautious_adam_step(P, G[t % 2], M, V, cfgs[t], muls)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    elems = aset.elements()
+    nbytes = elems * adam_bytes_per_element()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] cautious Adam: {ms:.4f} ms/step, {gbs:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    return {"workload": aset.name, "elements": elems,
+            "tensors": [f"{lab} {'x'.join(map(str, sh))} wd_mul {w:g}"
+                        for lab, sh, w in aset.tensors],
+            "dtype": "bf16 params and grads, fp32 moments, fp32 arithmetic",
+            "config": {"lr": lr, "betas": list(betas), "eps": eps, "weight_decay": wd},
+            "data": "synthetic (seeded GPU draws: N(0,0.02) params, N(0,1e-3) grads, "
+                    "2 staged batches)",
+            "steps": steps, "warmup": warmup, "ms_per_step": ms,
+            "launches_per_step": 1, "value": 1000.0 / ms, "unit": "Adam steps/s",
+            "roofline": {"kernel": "cautious_adam", "bound": "hbm", "achieved": gbs,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("cautious_adam", aset.name),
+                         "avg_launch_us": 1e3 * ms,
+                         "bytes_per_launch": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +184,9 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
+    ap.add_argument("--adam-only", action="store_true",
+                    help="time only the cautious-Adam step and print its JSON object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before timing, copy 256 MiB device to device once (a plain copy of "
                          "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -134,6 +199,14 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.adam_only:
+        if args.copy_calibration:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        print(json.dumps(bench_adam(args.steps, args.warmup, dev)), flush=True)
+        return
     wl = si.WORKLOADS[args.workload]
     n = wl.n
     print(f"[bench] {wl.name}: {n} matrices, {wl.elements() / 1e6:.1f} M elements, "
@@ -220,6 +293,12 @@ def main():
                                "traffic": measured_traffic(dom, wl.name),
                                "avg_launch_us": 1e3 * dms / max(dl, 1)}
 
+    plan.close()
+    if not args.no_adam:
+        del W, M, G
+        torch.cuda.empty_cache()
+        out["next_rows"] = {"cautious_adam": bench_adam(args.steps, args.warmup, dev)}
+
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)
@@ -227,7 +306,6 @@ def main():
                    "cpu_count": os.cpu_count(), "torch": torch.__version__,
                    "hip": torch.version.hip,
                    "gpu": torch.cuda.get_device_name(dev)}
-    plan.close()
     print(json.dumps(out), flush=True)
 
 

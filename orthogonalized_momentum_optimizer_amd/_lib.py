@@ -1,4 +1,5 @@
-"""ctypes binding of libmuon.so (the C ABI of include/muon.h), with the same names.
+"""ctypes binding of libmuon.so (the C ABI of include/muon.h and include/cautious_adam.h),
+with the same names.
 
 Only argument marshalling happens here: every step of the optimizer runs in the HIP
 kernels of the library. PyTorch's HIP runtime is loaded first (``import torch``) so the
@@ -32,6 +33,7 @@ EXPORTED = (
     "muon_config_default", "muon_plan_create", "muon_plan_workspace_size", "muon_step",
     "muon_newton_schulz", "muon_plan_destroy", "muon_plan_set_profiling",
     "muon_plan_read_profile", "muon_status_string", "muon_last_error",
+    "muon_adam_config_default", "muon_cautious_adam_step",
 )
 
 
@@ -65,6 +67,30 @@ class muon_config(ctypes.Structure):
         ("c", ctypes.c_float),
         ("eps", ctypes.c_float),
         ("schedule", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
+class muon_adam_tensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+        ("param_dtype", ctypes.c_int),
+        ("grad_dtype", ctypes.c_int),
+        ("wd_mul", ctypes.c_float),
+    ]
+
+
+class muon_adam_config(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("step", ctypes.c_int64),
     ]
 
 
@@ -102,6 +128,11 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_read_profile.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(i64), ctypes.c_int]
     L.muon_plan_read_profile.restype = ctypes.c_int
+    L.muon_adam_config_default.argtypes = [ctypes.POINTER(muon_adam_config)]
+    L.muon_adam_config_default.restype = None
+    L.muon_cautious_adam_step.argtypes = [ctypes.POINTER(muon_adam_tensor), i64,
+                                          ctypes.POINTER(muon_adam_config), vp]
+    L.muon_cautious_adam_step.restype = ctypes.c_int
     L.muon_status_string.argtypes = [ctypes.c_int]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_last_error.argtypes = []
@@ -188,4 +219,24 @@ def make_matrices(entries) -> ctypes.Array:
     arr = (muon_matrix * max(len(entries), 1))()
     for i, e in enumerate(entries):
         arr[i] = muon_matrix(*e)
+    return arr
+
+
+def muon_adam_config_default() -> muon_adam_config:
+    cfg = muon_adam_config()
+    lib().muon_adam_config_default(ctypes.byref(cfg))
+    return cfg
+
+
+def muon_cautious_adam_step(tensors, n: int, cfg: muon_adam_config, stream: int) -> None:
+    """``tensors``: a ctypes array of muon_adam_tensor (or None when n == 0)."""
+    _check(lib().muon_cautious_adam_step(tensors, n, ctypes.byref(cfg), stream))
+
+
+def make_adam_tensors(entries) -> ctypes.Array:
+    """entries: iterable of (param, grad, exp_avg, exp_avg_sq, numel, pdt, gdt, wd_mul)."""
+    entries = list(entries)
+    arr = (muon_adam_tensor * max(len(entries), 1))()
+    for i, e in enumerate(entries):
+        arr[i] = muon_adam_tensor(*e)
     return arr

@@ -1,4 +1,4 @@
-"""Builds libmuon.so (the HIP kernels and the C ABI of include/muon.h) for gfx950 in place.
+"""Builds libmuon.so (the HIP kernels and the C ABI of include/*.h) for gfx950 in place.
 
     python -m orthogonalized_momentum_optimizer_amd.build
 
@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip"]
+SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip",
+           "ns_apply_bf16.hip", "ns_gemm_f32.hip", "cautious_adam.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -83,7 +84,8 @@ def device_asm(src: str) -> str:
     out_dir = os.path.join(BUILD, "asm")
     os.makedirs(out_dir, exist_ok=True)
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)) + [os.path.join(INCLUDE, "muon.h")]:
+    headers = [os.path.join(INCLUDE, h) for h in sorted(os.listdir(INCLUDE))]
+    for name in sorted(os.listdir(CSRC)) + headers:
         path = name if os.path.isabs(name) else os.path.join(CSRC, name)
         with open(path, "rb") as f:
             h.update(f.read())

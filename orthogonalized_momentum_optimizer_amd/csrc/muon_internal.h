@@ -6,7 +6,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace muon {
+
+// Host-side error reporting shared by every entry point (muon_last_error reads it): fail
+// stores the formatted message for this thread and returns `code`.
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
+// A byte range of a buffer an entry point receives.
+struct Range {
+  uintptr_t lo, hi;
+  bool writable;
+};
+// MUON_OK, or MUON_ERR_INVALID_ARG when a written range overlaps any other range.
+int check_overlaps(std::vector<Range>& rs);
 
 constexpr int kPad = 128;        // wide shapes are padded to multiples of this
 constexpr int kTile = 64;        // elementwise kernels work on 64x64 tiles

@@ -22,8 +22,10 @@
 using namespace muon;
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace muon {
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -34,6 +36,26 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
+
+void clear_error() { g_last_error.clear(); }
+
+int check_overlaps(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  uintptr_t max_any = 0, max_w = 0;
+  for (const Range& r : rs) {
+    if (r.lo < max_w || (r.writable && r.lo < max_any))
+      return fail(MUON_ERR_INVALID_ARG,
+                  "buffer [%p, %p) overlaps another buffer of the call, and one of them is "
+                  "written", (void*)r.lo, (void*)r.hi);
+    max_any = std::max(max_any, r.hi);
+    if (r.writable) max_w = std::max(max_w, r.hi);
+  }
+  return MUON_OK;
+}
+
+}  // namespace muon
+
+namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int pad_up(int64_t x) { return (int)((x + kPad - 1) / kPad * kPad); }
@@ -50,11 +72,6 @@ struct Group {
   int mp = 0, np = 0, count = 0, tiles64 = 0;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0, off_scales = 0;
   std::vector<int> sets;
-};
-
-struct Range {
-  uintptr_t lo, hi;
-  bool writable;
 };
 
 }  // namespace
@@ -108,21 +125,6 @@ int check_workspace(const muon_plan* p, const void* ws, size_t bytes) {
     return fail(MUON_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
   if (bytes < p->ws_bytes)
     return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, p->ws_bytes);
-  return MUON_OK;
-}
-
-// Any overlap that involves a buffer the call writes is an error.
-int check_overlaps(std::vector<Range>& rs) {
-  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
-  uintptr_t max_any = 0, max_w = 0;
-  for (const Range& r : rs) {
-    if (r.lo < max_w || (r.writable && r.lo < max_any))
-      return fail(MUON_ERR_INVALID_ARG,
-                  "buffer [%p, %p) overlaps another buffer of the call, and one of them is "
-                  "written", (void*)r.lo, (void*)r.hi);
-    max_any = std::max(max_any, r.hi);
-    if (r.writable) max_w = std::max(max_w, r.hi);
-  }
   return MUON_OK;
 }
 
@@ -300,7 +302,7 @@ void muon_config_default(muon_config* cfg) {
 int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
                      const muon_dtype* param_dtype, const muon_dtype* grad_dtype, int64_t n,
                      muon_precision precision) {
-  g_last_error.clear();
+  clear_error();
   if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
@@ -393,7 +395,7 @@ size_t muon_plan_workspace_size(const muon_plan* plan) { return plan ? plan->ws_
 
 int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_config* cfg,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
   if (n != plan->n)
     return fail(MUON_ERR_INVALID_ARG, "n = %lld but the plan has %lld matrices", (long long)n,
@@ -457,7 +459,7 @@ int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_co
 int muon_newton_schulz(muon_plan* plan, const void* const* in, void* const* out, int64_t n,
                        const muon_config* cfg, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
   if (n != plan->n)
     return fail(MUON_ERR_INVALID_ARG, "n = %lld but the plan has %lld matrices", (long long)n,
@@ -495,7 +497,7 @@ void muon_plan_destroy(muon_plan* plan) {
 }
 
 int muon_plan_set_profiling(muon_plan* plan, int enable) {
-  g_last_error.clear();
+  clear_error();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
   if (plan->prof) {
     prof_collect(plan);
@@ -531,7 +533,7 @@ int muon_plan_set_profiling(muon_plan* plan, int enable) {
 }
 
 int muon_plan_read_profile(muon_plan* plan, double* ms, int64_t* launches, int nkinds) {
-  g_last_error.clear();
+  clear_error();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
   if (nkinds < 0 || (nkinds > 0 && (!ms || !launches)))
     return fail(MUON_ERR_INVALID_ARG, "ms and launches must hold nkinds entries");

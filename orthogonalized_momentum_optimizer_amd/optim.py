@@ -1,5 +1,6 @@
-"""PyTorch-facing wrappers of the C ABI: a plan holder, the Newton-Schulz function and the
-``Muon`` optimizer.
+"""PyTorch-facing wrappers of the C ABI: a plan holder, the Newton-Schulz function, the
+``Muon`` optimizer for the weight matrices and the ``CautiousAdam`` optimizer for the other
+parameters.
 
 The optimizer mirrors the constructor of page
 "深入解析KellerJordan/modded-nanogpt中的训练架构与优化技术" (section
@@ -209,4 +210,83 @@ class Muon(torch.optim.Optimizer):
             cfg = make_config(lr=group["lr"], beta=group["momentum"],
                               nesterov=group["nesterov"], ns_steps=group["ns_steps"])
             plan.step(params, grads, moms, cfg)
+        return loss
+
+
+def make_adam_config(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+                     step=1) -> L.muon_adam_config:
+    """A muon_adam_config; ``step`` is the index t >= 1 of the step in the bias corrections."""
+    cfg = L.muon_adam_config_default()
+    cfg.lr, cfg.beta1, cfg.beta2 = lr, betas[0], betas[1]
+    cfg.eps, cfg.weight_decay, cfg.step = eps, weight_decay, int(step)
+    return cfg
+
+
+def cautious_adam_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                       exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor],
+                       cfg: L.muon_adam_config, wd_muls: Optional[Sequence[float]] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> None:
+    """One cautious-Adam step of libmuon.so over contiguous CUDA tensors of any shape (p and g
+    bfloat16 or float32, the two moments float32 and zero before step 1)."""
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have the same length")
+    wd_muls = [1.0] * n if wd_muls is None else list(wd_muls)
+    if len(wd_muls) != n:
+        raise ValueError("one wd_mul per tensor")
+    ents = []
+    for i, (p, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        for t in (p, g, m, v):
+            if t.numel() != p.numel() or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"tensor {i}: contiguous CUDA tensors of {p.numel()} "
+                                 "elements expected")
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError(f"tensor {i}: exp_avg and exp_avg_sq must be float32")
+        ents.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel(),
+                     dtype_code(p.dtype), dtype_code(g.dtype), float(wd_muls[i])))
+    arr = L.make_adam_tensors(ents) if n else None
+    L.muon_cautious_adam_step(arr, n, cfg, _stream_handle(stream))
+
+
+class CautiousAdam(torch.optim.Optimizer):
+    """Adam with cautious (sign-masked, decoupled) weight decay for the non-matrix
+    parameters (embeddings, LM head, scalars), as in the record analysed at lqnn.cn,
+    section 3.3. Each parameter group may carry ``wd_mul``, the multiplier of the base
+    ``weight_decay`` for its tensors (the page's table uses 150 for embed / lm_head and 0 for
+    scalars). The whole step runs in libmuon.so, one fused pass per dtype pair."""
+
+    def __init__(self, params, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0, wd_mul: float = 1.0):
+        defaults = dict(lr=lr, betas=tuple(betas), eps=eps, weight_decay=weight_decay,
+                        wd_mul=wd_mul)
+        super().__init__(params, defaults)
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            by_step = {}
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if not p.is_contiguous() or not p.grad.is_contiguous():
+                    raise ValueError("CautiousAdam needs contiguous parameters and gradients")
+                st = self.state[p]
+                if "step" not in st:
+                    st["step"] = 0
+                    st["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                    st["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32,
+                                                   device=p.device)
+                st["step"] += 1
+                by_step.setdefault(st["step"], []).append(p)
+            for t, ps in by_step.items():
+                cfg = make_adam_config(group["lr"], group["betas"], group["eps"],
+                                       group["weight_decay"], t)
+                cautious_adam_step(ps, [p.grad for p in ps],
+                                   [self.state[p]["exp_avg"] for p in ps],
+                                   [self.state[p]["exp_avg_sq"] for p in ps], cfg,
+                                   [group["wd_mul"]] * len(ps))
         return loss

@@ -12,24 +12,27 @@ import torch
 from orthogonalized_momentum_optimizer_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "muon.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = sorted(os.path.join(INCLUDE, h) for h in os.listdir(INCLUDE) if h.endswith(".h"))
 
 no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
                                  reason="fake device addresses are only used without a GPU")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     lib = L.lib()
     names = declared_functions()
-    assert len(names) >= 10
+    assert len(names) >= 12 and "muon_cautious_adam_step" in names
     for name in names:
-        assert hasattr(lib, name), f"{name} is declared in muon.h but not exported"
+        assert hasattr(lib, name), f"{name} is declared in include/ but not exported"
     assert sorted(L.EXPORTED) == names
 
 
@@ -272,3 +275,92 @@ def test_step_rejects_with_real_buffers():
     plan.step([W], [G], [M], cfg)    # valid call still works afterwards
     torch.cuda.synchronize()
     plan.close()
+
+
+# ---- cautious Adam: defaults and validation ---------------------------------------------------
+
+def test_adam_config_default():
+    c = L.muon_adam_config_default()
+    assert (round(c.lr, 9), round(c.beta1, 6), round(c.beta2, 6)) == (1e-3, 0.9, 0.999)
+    assert abs(c.eps - 1e-8) < 1e-15 and c.weight_decay == 0.0 and c.step == 1
+
+
+def test_adam_empty_call_is_a_no_op():
+    L.muon_cautious_adam_step(None, 0, L.muon_adam_config_default(), 0)
+
+
+def _adam_fake_call(mutate=None, cfg_mut=None, n=None):
+    ents = []
+    addr = BASE
+    for numel, pdt in ((1000, 0), (37, 1)):
+        ents.append([addr, addr + (1 << 20), addr + (2 << 20), addr + (3 << 20), numel, pdt, 0,
+                     1.0])
+        addr += 4 << 20
+    if mutate:
+        mutate(ents)
+    arr = L.make_adam_tensors([tuple(e) for e in ents])
+    cfg = L.muon_adam_config_default()
+    if cfg_mut:
+        cfg_mut(cfg)
+    with pytest.raises(L.MuonError) as e:
+        L.muon_cautious_adam_step(arr, len(ents) if n is None else n, cfg, 0)
+    return e.value.status, L.muon_last_error()
+
+
+@no_gpu_only
+@pytest.mark.parametrize("case,code", [
+    ("null_param", L.MUON_ERR_INVALID_ARG),
+    ("null_exp_avg_sq", L.MUON_ERR_INVALID_ARG),
+    ("misaligned_grad", L.MUON_ERR_INVALID_ARG),
+    ("negative_numel", L.MUON_ERR_INVALID_ARG),
+    ("huge_numel", L.MUON_ERR_UNSUPPORTED),
+    ("bad_dtype", L.MUON_ERR_INVALID_ARG),
+    ("nan_wd_mul", L.MUON_ERR_INVALID_ARG),
+    ("param_overlaps_grad", L.MUON_ERR_INVALID_ARG),
+    ("exp_avg_overlaps_other_param", L.MUON_ERR_INVALID_ARG),
+    ("moments_alias", L.MUON_ERR_INVALID_ARG),
+    ("negative_n", L.MUON_ERR_INVALID_ARG),
+])
+def test_adam_rejects_tensors(case, code):
+    def mutate(e):
+        if case == "null_param": e[0][0] = 0
+        if case == "null_exp_avg_sq": e[1][3] = 0
+        if case == "misaligned_grad": e[1][1] += 4
+        if case == "negative_numel": e[0][4] = -1
+        if case == "huge_numel": e[0][4] = (1 << 40) + 1
+        if case == "bad_dtype": e[1][6] = 3
+        if case == "nan_wd_mul": e[0][7] = float("nan")
+        if case == "param_overlaps_grad": e[0][1] = e[0][0] + 16
+        if case == "exp_avg_overlaps_other_param": e[1][2] = e[0][0] + 32
+        if case == "moments_alias": e[0][3] = e[0][2]
+    status, msg = _adam_fake_call(mutate, n=-1 if case == "negative_n" else None)
+    assert status == code and msg
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,value", [("lr", float("nan")), ("eps", -1e-8),
+                                         ("eps", float("inf")), ("beta1", 1.0),
+                                         ("beta2", -0.1), ("beta1", float("nan")),
+                                         ("weight_decay", float("inf")), ("step", 0)])
+def test_adam_rejects_config(field, value):
+    status, msg = _adam_fake_call(cfg_mut=lambda c: setattr(c, field, value))
+    assert status == L.MUON_ERR_INVALID_ARG and msg
+
+
+@no_gpu_only
+def test_adam_decay_overflow_rejected():
+    def mutate(e):
+        e[0][7] = 3e38
+    status, msg = _adam_fake_call(mutate, cfg_mut=lambda c: setattr(c, "weight_decay", 10.0))
+    assert status == L.MUON_ERR_INVALID_ARG and "overflows" in msg
+
+
+@no_gpu_only
+def test_adam_validation_passes_for_legal_sets():
+    """Empty tensors may carry NULL pointers, and tensors may share one read-only gradient:
+    such calls pass validation and fail only when they launch (there is no GPU here)."""
+    def mutate(e):
+        e[1][1] = e[0][1]
+        e.append([0, 0, 0, 0, 0, 0, 0, 1.0])
+    status, msg = _adam_fake_call(mutate)
+    assert status == L.MUON_ERR_HIP, msg
