@@ -16,10 +16,11 @@ Sources (the pages are cited by title and section):
   中的退火行 RMS 缩放 Langevin/SGLD 探索噪声", which names Frobenius normalisation as the
   step in front of the quintic maps of the Muon family; and section 3.3 "bigram 与
   value-embedding 银行上的 C-Optim / 谨慎 Adam" (cautious Adam for the embedding-like
-  parameters, oracle/cautious_adam.py).
+  parameters, oracle/cautious_adam.py); section 3.2 also names NorMuon's per-lane energy
+  equaliser after the orthogonalisation (oracle/row_equalizer.py).
 
-Readings where the pages are silent are listed in the headers of muon.py and
-cautious_adam.py.
+Readings where the pages are silent are listed in the headers of muon.py,
+cautious_adam.py and row_equalizer.py.
 """
 from .muon import (  # noqa: F401
     DEFAULT_ABC,
@@ -36,4 +37,10 @@ from .cautious_adam import (  # noqa: F401
     cautious_decay,
     cautious_adam_step,
     cautious_adam_run,
+)
+from .row_equalizer import (  # noqa: F401
+    row_second_moment,
+    row_equalize,
+    muon_step_equalized,
+    muon_run_equalized,
 )
