@@ -23,6 +23,13 @@
  *   if rows > cols the iteration runs on X^T (wide form) and the result is transposed back
  *   ns_steps rounds of the quintic iteration above
  *   W <- W - lr * O                                  (O = the iteration's result)
+ * With cfg->row_equalize set, O is first passed through a per-row energy equaliser (the
+ * record analysis at lqnn.cn, section 3.2, names NorMuon's per-lane energy equaliser, an
+ * Adafactor-style variance estimate, after the orthogonalisation; it prints no formula, so
+ * this is the plainest reading): with v the matrix's per-row state (rows fp32 values),
+ *   v_i <- row_beta * v_i + (1 - row_beta) * mean_j O_ij^2      (rows of the caller's layout)
+ *   D_ij = O_ij / (sqrt(v_i) + row_eps)
+ *   O   <- D * ||O||_F / ||D||_F                     (total energy kept; 0 stays 0)
  *
  * Conventions shared by every entry point:
  *   - All buffers are device memory on the current HIP device, row-major, contiguous, with
@@ -70,7 +77,11 @@ typedef enum { MUON_NS_BF16 = 0, MUON_NS_F32_DEBUG = 1 } muon_precision;
  *   grad        rows x cols, grad_dtype, read only
  *   momentum    rows x cols fp32, updated in place; zero-fill it before the first step
  *   update_out  NULL, or rows x cols fp32 that receives O (the orthogonalised update, in the
- *               matrix's own orientation, before the lr scaling)
+ *               matrix's own orientation, before the lr scaling; the equalised O when
+ *               cfg->row_equalize is set)
+ *   row_var     NULL, or rows fp32: the row equaliser's per-row state v, updated in place;
+ *               zero-fill it before the first step. Required when cfg->row_equalize is set,
+ *               ignored otherwise.
  * rows, cols and the dtypes must equal the plan's entry at the same index. */
 typedef struct {
   void *param;
@@ -81,6 +92,7 @@ typedef struct {
   int64_t cols;
   muon_dtype param_dtype;
   muon_dtype grad_dtype;
+  float *row_var;
 } muon_matrix;
 
 /* Hyper-parameters of a step. lr, beta (momentum), nesterov and ns_steps follow the
@@ -92,7 +104,10 @@ typedef struct {
  * {a_k, b_k, c_k}, k = 0..ns_steps-1, one quintic per round: the mechanism behind the record
  * analysed at lqnn.cn (section 3.2), which replaces the fixed quintic by a cascade of
  * re-derived quintic maps (the pages do not print their values, so they are the caller's).
- * The array is read during the call only; every value must be finite. */
+ * The array is read during the call only; every value must be finite.
+ *
+ * row_equalize: 0, or 1 to apply the per-row energy equaliser above to O before the update
+ * (muon_step only), with row_beta in [0, 1) and finite row_eps >= 0. */
 typedef struct {
   float lr;
   float beta;
@@ -101,10 +116,14 @@ typedef struct {
   float a, b, c;
   float eps;
   const float *schedule;
+  int row_equalize;
+  float row_beta;
+  float row_eps;
 } muon_config;
 
 /* Fills cfg with lr 0.02, beta 0.95, nesterov 1, ns_steps 5, (3.4445, -4.7750, 2.0315),
- * eps 1e-7, schedule NULL. A NULL cfg is ignored. */
+ * eps 1e-7, schedule NULL, row_equalize 0, row_beta 0.95, row_eps 1e-8. A NULL cfg is
+ * ignored. */
 void muon_config_default(muon_config *cfg);
 
 /* Builds a plan for n matrices (n >= 0) of the given shapes and dtypes. The plan groups the
@@ -128,7 +147,8 @@ int muon_step(muon_plan *plan, const muon_matrix *mats, int64_t n, const muon_co
 /* The orthogonalisation alone (no momentum, no parameter update), for in[i] (rows x cols of
  * grad_dtype) into out[i] (rows x cols of param_dtype): out = NS(in / (||in||_F + eps)) with
  * cfg's ns_steps, a, b, c and eps; cfg's lr, beta and nesterov are ignored. This is the
- * pages' zeropower_via_newtonschulz5 with the pre-normalisation applied. */
+ * pages' zeropower_via_newtonschulz5 with the pre-normalisation applied; row_equalize is
+ * ignored. */
 int muon_newton_schulz(muon_plan *plan, const void *const *in, void *const *out, int64_t n,
                        const muon_config *cfg, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
@@ -149,7 +169,8 @@ typedef enum {
   MUON_KERNEL_POLY = 3,     /* B = b A + c A A (upper tiles + mirror)         */
   MUON_KERNEL_APPLY = 4,    /* X' = s (a X + B X)                             */
   MUON_KERNEL_UPDATE = 5,   /* W -= lr O (and O out)                          */
-  MUON_KERNEL_KINDS = 6
+  MUON_KERNEL_ROWEQ = 6,    /* row equaliser: row sums of O^2, per-row factors */
+  MUON_KERNEL_KINDS = 7
 } muon_kernel_kind;
 
 /* Waits for the recorded events and writes, per kind (up to nkinds entries), the summed

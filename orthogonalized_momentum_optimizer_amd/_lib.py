@@ -27,7 +27,7 @@ MUON_DT_F32 = 1
 MUON_NS_BF16 = 0
 MUON_NS_F32_DEBUG = 1
 
-KERNEL_KINDS = ("momentum", "norm", "gram", "poly", "apply", "update")
+KERNEL_KINDS = ("momentum", "norm", "gram", "poly", "apply", "update", "roweq")
 
 EXPORTED = (
     "muon_config_default", "muon_plan_create", "muon_plan_workspace_size", "muon_step",
@@ -53,6 +53,7 @@ class muon_matrix(ctypes.Structure):
         ("cols", ctypes.c_int64),
         ("param_dtype", ctypes.c_int),
         ("grad_dtype", ctypes.c_int),
+        ("row_var", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +68,9 @@ class muon_config(ctypes.Structure):
         ("c", ctypes.c_float),
         ("eps", ctypes.c_float),
         ("schedule", ctypes.POINTER(ctypes.c_float)),
+        ("row_equalize", ctypes.c_int),
+        ("row_beta", ctypes.c_float),
+        ("row_eps", ctypes.c_float),
     ]
 
 
@@ -214,7 +218,8 @@ def muon_plan_read_profile(plan: int) -> dict:
 
 
 def make_matrices(entries) -> ctypes.Array:
-    """entries: iterable of (param_ptr, grad_ptr, momentum_ptr, out_ptr, rows, cols, pdt, gdt)."""
+    """entries: iterable of (param_ptr, grad_ptr, momentum_ptr, out_ptr, rows, cols, pdt, gdt
+    [, row_var_ptr])."""
     entries = list(entries)
     arr = (muon_matrix * max(len(entries), 1))()
     for i, e in enumerate(entries):

@@ -46,12 +46,22 @@ struct ElemLaunch {
   int nesterov;
   float lr;
   int apply_scale;                 // update: multiply X by s1 (ns_steps == 0)
+  // row equaliser (per-slot arrays of np floats, slot0-based; nullptr = not used)
+  float* rowvar[kMaxPerLaunch];    // finish: the caller's per-row state v
+  float* rowsum;                   // rowstat: out; finish: in (sums of O^2 per row)
+  float* rowf;                     // finish: out; update: per-row factor of O
+  float row_beta, row_eps;
 };
 
 // dtype codes: 0 = bf16, 1 = f32 (match muon_dtype)
 hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStream_t s);
 hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_param_dt, int x_f32,
                          hipStream_t s);
+// Row equaliser: rowstat writes each row's sum of O^2 (O in the caller's orientation, s1
+// applied when apply_scale); finish updates the caller's row state and writes the per-row
+// factors gamma / (sqrt(v_i) + eps) that the update kernel applies to O.
+hipError_t launch_rowstat(const ElemLaunch& L, int x_f32, hipStream_t s);
+hipError_t launch_roweq_finish(const ElemLaunch& L, hipStream_t s);
 // Per-matrix norm finish: scales[4*i] = 1/(nu+eps), [4*i+1] = that squared, [4*i+2] = nu.
 hipError_t launch_norm(const float* partials, int tiles_per_mat, float* scales, int count,
                        float eps, hipStream_t s);

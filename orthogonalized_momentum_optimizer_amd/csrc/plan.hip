@@ -71,6 +71,7 @@ struct LaunchSet {  // matrices of one shape and dtype pair, contiguous slots of
 struct Group {
   int mp = 0, np = 0, count = 0, tiles64 = 0;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0, off_scales = 0;
+  size_t off_rowsum = 0, off_rowf = 0;  // row equaliser: count x np floats each
   std::vector<int> sets;
 };
 
@@ -88,6 +89,7 @@ struct muon_plan {
   std::vector<muon_matrix> checked_mats;
   std::vector<const void*> checked_ptrs;
   const void* checked_ws = nullptr;
+  bool checked_roweq = false;
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> ev;  // pairs (start, stop)
@@ -115,6 +117,14 @@ int check_cfg(const muon_config* cfg, bool momentum) {
     for (int k = 0; k < 3 * cfg->ns_steps; ++k)
       if (!finite(cfg->schedule[k]))
         return fail(MUON_ERR_INVALID_ARG, "schedule entry %d is not finite", k);
+  if (momentum && cfg->row_equalize) {
+    if (cfg->row_equalize != 1)
+      return fail(MUON_ERR_INVALID_ARG, "row_equalize = %d (0 or 1)", cfg->row_equalize);
+    if (!(cfg->row_beta >= 0.f && cfg->row_beta < 1.f))
+      return fail(MUON_ERR_INVALID_ARG, "row_beta must lie in [0, 1)");
+    if (!finite(cfg->row_eps) || cfg->row_eps < 0.f)
+      return fail(MUON_ERR_INVALID_ARG, "row_eps must be finite and >= 0");
+  }
   return MUON_OK;
 }
 
@@ -179,8 +189,8 @@ struct Launcher {
 // phase); params: W (nullable array = no update); outs: O destination (nullable entries);
 // out_param_dtype: O is written in the param dtype (else fp32).
 int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* const* params,
-            void* const* outs, bool out_param_dtype, const muon_config* cfg, void* ws,
-            hipStream_t stream) {
+            void* const* outs, float* const* row_vars, bool out_param_dtype,
+            const muon_config* cfg, void* ws, hipStream_t stream) {
   prof_collect(p);
   Launcher L{p, stream};
   const bool f32 = p->prec == MUON_NS_F32_DEBUG;
@@ -249,8 +259,36 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
       std::swap(N.x_in, N.x_out);
     }
 
-    // phase 3: parameter update (and O output)
+    // phase 3: row equaliser (optional), parameter update (and O output)
     char* xres = static_cast<char*>(N.x_in);
+    float* rowsum = reinterpret_cast<float*>(base + G.off_rowsum);
+    float* rowf = reinterpret_cast<float*>(base + G.off_rowf);
+    if (row_vars) {
+      for (int si : G.sets) {
+        const LaunchSet& S = p->sets[si];
+        for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
+          ElemLaunch E{};
+          E.count = (int)std::min<size_t>(kMaxPerLaunch, S.mats.size() - q0);
+          for (int q = 0; q < E.count; ++q) E.rowvar[q] = row_vars[S.mats[q0 + q]];
+          E.rows = S.rows;
+          E.cols = S.cols;
+          E.tall = S.rows > S.cols;
+          E.mp = G.mp;
+          E.np = G.np;
+          const int slot = S.slot0 + (int)q0;
+          E.x = xres + (size_t)slot * xslot;
+          E.scales = scales + 4 * (size_t)slot;
+          E.apply_scale = cfg->ns_steps == 0;
+          E.rowsum = rowsum + (size_t)slot * G.np;
+          E.rowf = rowf + (size_t)slot * G.np;
+          E.row_beta = cfg->row_beta;
+          E.row_eps = cfg->row_eps;
+          L.run(MUON_KERNEL_ROWEQ, "row sums", [&] { return launch_rowstat(E, f32, stream); });
+          L.run(MUON_KERNEL_ROWEQ, "row factors",
+                [&] { return launch_roweq_finish(E, stream); });
+        }
+      }
+    }
     for (int si : G.sets) {
       const LaunchSet& S = p->sets[si];
       for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
@@ -272,6 +310,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
         E.scales = scales + 4 * (size_t)slot;
         E.apply_scale = cfg->ns_steps == 0;
         E.lr = cfg->lr;
+        E.rowf = row_vars ? rowf + (size_t)slot * G.np : nullptr;
         const int out_dt = out_param_dtype ? (S.pdt == MUON_DT_F32) : 1;
         L.run(MUON_KERNEL_UPDATE, "update",
               [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
@@ -297,6 +336,9 @@ void muon_config_default(muon_config* cfg) {
   cfg->c = 2.0315f;
   cfg->eps = 1e-7f;
   cfg->schedule = nullptr;
+  cfg->row_equalize = 0;
+  cfg->row_beta = 0.95f;
+  cfg->row_eps = 1e-8f;
 }
 
 int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
@@ -384,6 +426,8 @@ int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
     G.off_b = off; off = align256(off + as);
     G.off_part = off; off = align256(off + (size_t)G.count * G.tiles64 * 4);
     G.off_scales = off; off = align256(off + (size_t)G.count * 16);
+    G.off_rowsum = off; off = align256(off + (size_t)G.count * G.np * 4);
+    G.off_rowf = off; off = align256(off + (size_t)G.count * G.np * 4);
   }
   p->ws_bytes = off;
 
@@ -405,7 +449,9 @@ int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_co
   if (!mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
   if (int st = check_workspace(plan, workspace, workspace_bytes)) return st;
 
-  const bool same = plan->checked_ws == workspace && plan->checked_mats.size() == (size_t)n &&
+  const bool roweq = cfg->row_equalize != 0;
+  const bool same = plan->checked_ws == workspace && plan->checked_roweq == roweq &&
+                    plan->checked_mats.size() == (size_t)n &&
                     std::memcmp(plan->checked_mats.data(), mats, sizeof(muon_matrix) * n) == 0;
   if (!same) {
     std::vector<Range> rs;
@@ -422,8 +468,12 @@ int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_co
         return fail(MUON_ERR_INVALID_ARG, "matrix %lld: param, grad and momentum must be non-NULL",
                     (long long)i);
       if (!aligned16(M.param) || !aligned16(M.grad) || !aligned16(M.momentum) ||
-          (M.update_out && !aligned16(M.update_out)))
+          (M.update_out && !aligned16(M.update_out)) || (roweq && !aligned16(M.row_var)))
         return fail(MUON_ERR_INVALID_ARG, "matrix %lld: buffers must be 16-byte aligned",
+                    (long long)i);
+      if (roweq && !M.row_var)
+        return fail(MUON_ERR_INVALID_ARG,
+                    "matrix %lld: row_var must be non-NULL when row_equalize is set",
                     (long long)i);
       const size_t elems = (size_t)M.rows * M.cols;
       auto add = [&](const void* ptr, size_t bytes, bool w) {
@@ -434,6 +484,7 @@ int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_co
       add(M.grad, elems * dt_size(M.grad_dtype), false);
       add(M.momentum, elems * 4, true);
       if (M.update_out) add(M.update_out, elems * 4, true);
+      if (roweq) add(M.row_var, (size_t)M.rows * 4, true);
     }
     if (plan->ws_bytes) rs.push_back({reinterpret_cast<uintptr_t>(workspace),
                                       reinterpret_cast<uintptr_t>(workspace) + plan->ws_bytes,
@@ -441,19 +492,21 @@ int muon_step(muon_plan* plan, const muon_matrix* mats, int64_t n, const muon_co
     if (int st = check_overlaps(rs)) return st;
     plan->checked_mats.assign(mats, mats + n);
     plan->checked_ws = workspace;
+    plan->checked_roweq = roweq;
   }
 
   std::vector<const void*> grads(n);
-  std::vector<float*> moms(n);
+  std::vector<float*> moms(n), row_vars(n);
   std::vector<void*> params(n), outs(n);
   for (int64_t i = 0; i < n; ++i) {
     grads[i] = mats[i].grad;
     moms[i] = mats[i].momentum;
     params[i] = mats[i].param;
     outs[i] = mats[i].update_out;
+    row_vars[i] = mats[i].row_var;
   }
-  return enqueue(plan, grads.data(), moms.data(), params.data(), outs.data(), false, cfg,
-                 workspace, stream);
+  return enqueue(plan, grads.data(), moms.data(), params.data(), outs.data(),
+                 roweq ? row_vars.data() : nullptr, false, cfg, workspace, stream);
 }
 
 int muon_newton_schulz(muon_plan* plan, const void* const* in, void* const* out, int64_t n,
@@ -484,7 +537,7 @@ int muon_newton_schulz(muon_plan* plan, const void* const* in, void* const* out,
     rs.push_back({reinterpret_cast<uintptr_t>(workspace),
                   reinterpret_cast<uintptr_t>(workspace) + plan->ws_bytes, true});
   if (int st = check_overlaps(rs)) return st;
-  return enqueue(plan, in, nullptr, nullptr, out, true, cfg, workspace, stream);
+  return enqueue(plan, in, nullptr, nullptr, out, nullptr, true, cfg, workspace, stream);
 }
 
 void muon_plan_destroy(muon_plan* plan) {

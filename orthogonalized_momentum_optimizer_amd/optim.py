@@ -29,12 +29,15 @@ def dtype_code(dt: torch.dtype) -> int:
 
 
 def make_config(lr=0.02, beta=0.95, nesterov=True, ns_steps=5, abc=(3.4445, -4.7750, 2.0315),
-                eps=1e-7, schedule=None) -> L.muon_config:
-    """A muon_config. ``schedule``: None, or ns_steps (a, b, c) triples, one per round."""
+                eps=1e-7, schedule=None, row_equalize=False, row_beta=0.95,
+                row_eps=1e-8) -> L.muon_config:
+    """A muon_config. ``schedule``: None, or ns_steps (a, b, c) triples, one per round.
+    ``row_equalize``: apply the per-row energy equaliser (state buffers passed to the step)."""
     cfg = L.muon_config_default()
     cfg.lr, cfg.beta, cfg.nesterov, cfg.ns_steps = lr, beta, int(bool(nesterov)), int(ns_steps)
     cfg.a, cfg.b, cfg.c = abc
     cfg.eps = eps
+    cfg.row_equalize, cfg.row_beta, cfg.row_eps = int(bool(row_equalize)), row_beta, row_eps
     if schedule is not None:
         flat = [float(x) for triple in schedule for x in triple]
         if len(flat) != 3 * int(ns_steps):
@@ -82,14 +85,16 @@ class MuonPlan:
         except Exception:
             pass
 
-    def _matrices(self, params, grads, moms, outs):
+    def _matrices(self, params, grads, moms, outs, row_vars=None):
         n = len(self.shapes)
         outs = outs if outs is not None else [None] * n
-        key = tuple((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0)
-                    for p, g, m, o in zip(params, grads, moms, outs))
+        row_vars = row_vars if row_vars is not None else [None] * n
+        key = tuple((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
+                     v.data_ptr() if v is not None else 0)
+                    for p, g, m, o, v in zip(params, grads, moms, outs, row_vars))
         if key != self._mats_key:
             ents = []
-            for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
+            for i, (p, g, m, o, v) in enumerate(zip(params, grads, moms, outs, row_vars)):
                 r, c = self.shapes[i]
                 for t in (p, g, m) + ((o,) if o is not None else ()):
                     if tuple(t.shape) != (r, c) or not t.is_contiguous() or not t.is_cuda:
@@ -97,9 +102,14 @@ class MuonPlan:
                                          f"{r}x{c} (got {tuple(t.shape)})")
                 if m.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
                     raise TypeError(f"matrix {i}: momentum and update_out must be float32")
+                if v is not None and (v.numel() != r or v.dtype != torch.float32 or
+                                      not v.is_contiguous() or not v.is_cuda):
+                    raise ValueError(f"matrix {i}: row_var must be a contiguous CUDA float32 "
+                                     f"tensor of {r} elements")
                 ents.append((p.data_ptr(), g.data_ptr(), m.data_ptr(),
                              o.data_ptr() if o is not None else None, r, c,
-                             dtype_code(p.dtype), dtype_code(g.dtype)))
+                             dtype_code(p.dtype), dtype_code(g.dtype),
+                             v.data_ptr() if v is not None else None))
             self._mats = L.make_matrices(ents)
             self._mats_key = key
         return self._mats
@@ -113,11 +123,16 @@ class MuonPlan:
     def step(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
              moms: Sequence[torch.Tensor], cfg: L.muon_config,
              outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
-             stream: Optional[torch.cuda.Stream] = None) -> None:
+             stream: Optional[torch.cuda.Stream] = None,
+             row_vars: Optional[Sequence[torch.Tensor]] = None) -> None:
+        """``row_vars``: per matrix a float32 tensor of ``rows`` elements (the row equaliser's
+        state), needed when ``cfg.row_equalize`` is set."""
         n = len(self.shapes)
         if not (len(params) == len(grads) == len(moms) == n):
             raise ValueError(f"expected {n} params, grads and momentum buffers")
-        mats = self._matrices(params, grads, moms, outs) if n else None
+        if row_vars is not None and len(row_vars) != n:
+            raise ValueError(f"expected {n} row_var buffers")
+        mats = self._matrices(params, grads, moms, outs, row_vars) if n else None
         L.muon_step(self.handle, mats, n, cfg, self.workspace.data_ptr(), self.ws_bytes,
                     _stream_handle(stream))
 
@@ -157,11 +172,15 @@ class Muon(torch.optim.Optimizer):
     """Muon: SGD-Nesterov momentum orthogonalised by Newton-Schulz, for 2-D (or stacked
     >= 3-D) weight matrices. Each >= 3-D parameter is treated as a stack of matrices over
     its last two dimensions. 1-D parameters are rejected (they belong to another optimizer).
+    ``row_equalize`` adds the per-row energy equaliser of the NorMuon family between the
+    orthogonalisation and the update (state: one float per row of every matrix).
     """
 
     def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, nesterov: bool = True,
-                 ns_steps: int = 5, precision: str = "bf16"):
-        defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, ns_steps=ns_steps)
+                 ns_steps: int = 5, precision: str = "bf16", row_equalize: bool = False,
+                 row_beta: float = 0.95, row_eps: float = 1e-8):
+        defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, ns_steps=ns_steps,
+                        row_equalize=row_equalize, row_beta=row_beta, row_eps=row_eps)
         super().__init__(params, defaults)
         if precision not in _PREC:
             raise ValueError(f"precision must be one of {sorted(_PREC)}")
@@ -186,7 +205,7 @@ class Muon(torch.optim.Optimizer):
             with torch.enable_grad():
                 loss = closure()
         for gi, group in enumerate(self.param_groups):
-            params, grads, moms = [], [], []
+            params, grads, moms, rvars = [], [], [], []
             for p in group["params"]:
                 if p.grad is None:
                     continue
@@ -199,6 +218,12 @@ class Muon(torch.optim.Optimizer):
                 params += self._split(p)
                 grads += self._split(p.grad)
                 moms += self._split(st["momentum_buffer"])
+                if group["row_equalize"]:
+                    if "row_var" not in st:
+                        st["row_var"] = torch.zeros(p.shape[:-1], dtype=torch.float32,
+                                                    device=p.device)
+                    rv = st["row_var"]
+                    rvars += [rv] if rv.dim() == 1 else list(rv.reshape(-1, rv.shape[-1]))
             if not params:
                 continue
             key = (gi, tuple((tuple(x.shape), x.dtype, g.dtype) for x, g in zip(params, grads)))
@@ -208,8 +233,10 @@ class Muon(torch.optim.Optimizer):
                                 [g.dtype for g in grads], self.precision, params[0].device)
                 self._plans[key] = plan
             cfg = make_config(lr=group["lr"], beta=group["momentum"],
-                              nesterov=group["nesterov"], ns_steps=group["ns_steps"])
-            plan.step(params, grads, moms, cfg)
+                              nesterov=group["nesterov"], ns_steps=group["ns_steps"],
+                              row_equalize=group["row_equalize"], row_beta=group["row_beta"],
+                              row_eps=group["row_eps"])
+            plan.step(params, grads, moms, cfg, row_vars=rvars if group["row_equalize"] else None)
         return loss
 
 

@@ -47,6 +47,7 @@ def test_config_default():
     assert (round(c.lr, 6), round(c.beta, 6), c.nesterov, c.ns_steps) == (0.02, 0.95, 1, 5)
     assert (round(c.a, 4), round(c.b, 4), round(c.c, 4)) == (3.4445, -4.775, 2.0315)
     assert abs(c.eps - 1e-7) < 1e-12
+    assert c.row_equalize == 0 and abs(c.row_beta - 0.95) < 1e-7 and abs(c.row_eps - 1e-8) < 1e-15
 
 
 def test_status_strings():
@@ -57,7 +58,8 @@ def test_status_strings():
 
 def _ws_expected(shapes, esz):
     """Workspace layout: per padded wide group X0, X1 (count*mp*np), A, B (count*mp*mp),
-    partial sums (count * 64x64 tiles of X), scales (16 B per matrix), each 256-aligned."""
+    partial sums (count * 64x64 tiles of X), scales (16 B per matrix), row sums and row
+    factors of the row equaliser (count*np floats each), each 256-aligned."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     groups = {}
     for r, c in shapes:
@@ -72,6 +74,8 @@ def _ws_expected(shapes, esz):
         tot = al(tot + cnt * mp * mp * esz)
         tot = al(tot + cnt * (mp // 64) * (np_ // 64) * 4)
         tot = al(tot + cnt * 16)
+        tot = al(tot + cnt * np_ * 4)
+        tot = al(tot + cnt * np_ * 4)
     return tot
 
 
@@ -133,7 +137,7 @@ def _fake_call(mutate=None, cfg_mut=None, ws_off=0, ws_bytes=None, n=None):
     ents = []
     addr = BASE
     for r, c in shapes:
-        e = [addr, addr + (1 << 20), addr + (2 << 20), 0, r, c, 0, 0]
+        e = [addr, addr + (1 << 20), addr + (2 << 20), 0, r, c, 0, 0, addr + (3 << 20)]
         addr += 4 << 20
         ents.append(e)
     if mutate:
@@ -220,6 +224,37 @@ def test_make_config_schedule_length():
     cfg = make_config(ns_steps=2, schedule=[(1.0, 2.0, 3.0), (4.0, 5.0, 6.0)])
     assert [cfg.schedule[k] for k in range(6)] == [1.0, 2.0, 3.0, 4.0, 5.0, 6.0]
     assert not make_config().schedule
+
+
+@no_gpu_only
+@pytest.mark.parametrize("case", ["null_row_var", "misaligned_row_var", "row_var_overlaps_param",
+                                  "row_var_overlaps_other_row_var", "bad_row_beta",
+                                  "negative_row_eps", "nan_row_eps", "row_equalize_2"])
+def test_step_rejects_row_equaliser_arguments(case):
+    def mutate(e):
+        if case == "null_row_var": e[1][8] = 0
+        if case == "misaligned_row_var": e[0][8] += 4
+        if case == "row_var_overlaps_param": e[0][8] = e[0][0] + 16
+        if case == "row_var_overlaps_other_row_var": e[1][8] = e[0][8] + 128
+    def cfg_mut(c):
+        c.row_equalize = 2 if case == "row_equalize_2" else 1
+        if case == "bad_row_beta": c.row_beta = 1.0
+        if case == "negative_row_eps": c.row_eps = -1.0
+        if case == "nan_row_eps": c.row_eps = float("nan")
+    status, msg = _fake_call(mutate, cfg_mut)
+    assert status == L.MUON_ERR_INVALID_ARG and msg
+
+
+@no_gpu_only
+def test_row_state_checked_only_when_equalising():
+    """Without row_equalize a NULL or overlapping row_var is ignored (the call then fails only
+    at launch, there is no GPU here); with it, a valid set passes validation too."""
+    def mutate(e):
+        e[0][8] = 0
+        e[1][8] = e[1][0]
+    assert _fake_call(mutate)[0] == L.MUON_ERR_HIP
+    status, msg = _fake_call(cfg_mut=lambda c: setattr(c, "row_equalize", 1))
+    assert status == L.MUON_ERR_HIP, msg
 
 
 @no_gpu_only
