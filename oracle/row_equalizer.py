@@ -13,7 +13,8 @@ the readings below are the plainest ones its description supports:
 * N2 the variance estimate is a rank-1 (per-row) exponential moving average of the mean
   square of the orthogonalised update O: v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2,
   kept in an fp32 state buffer of one value per row (zero before the first step);
-* N3 each row is divided by its estimated RMS: D_ij = O_ij / (sqrt(v_i) + eps);
+* N3 each row is divided by its estimated RMS: D_ij = O_ij / (sqrt(v_i) + eps); with
+  eps = 0 a row whose state is 0 (its O row, a mean of squares, is then all zero) stays 0;
 * N4 an energy equaliser moves energy between lanes without changing the total: the result
   is D rescaled to O's Frobenius norm, O'_ij = D_ij ||O||_F / ||D||_F (0 when O is 0);
   a uniform factor on v (such as a bias correction) therefore cancels, up to eps;
@@ -41,7 +42,9 @@ def row_equalize(O, v, beta2: float = DEFAULT_ROW_BETA, eps: float = DEFAULT_ROW
     """[N2-N4] Returns (O', v') for an update O (rows x cols) and the row state v (rows)."""
     O = np.asarray(O, dtype=np.float64)
     v_new = row_second_moment(O, np.asarray(v, dtype=np.float64), beta2)
-    D = O / (np.sqrt(v_new)[:, None] + eps)
+    den = np.sqrt(v_new)[:, None] + eps
+    # [N3] a row whose denominator is 0 has v' = 0, so the row of O is zero and stays zero
+    D = np.divide(O, den, out=np.zeros_like(O), where=den > 0)
     e_o = float(np.sqrt(np.sum(O * O)))
     e_d = float(np.sqrt(np.sum(D * D)))
     return (D * (e_o / e_d) if e_d > 0 else np.zeros_like(O)), v_new

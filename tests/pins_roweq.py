@@ -95,10 +95,15 @@ def pin_e5_equivariance():
 
 
 def pin_e6_zero_update():
-    """A zero update stays zero and the state decays by beta2."""
+    """A zero update stays zero and the state decays by beta2; with eps 0, a zero row with a
+    zero state stays zero while the other rows keep all the energy: [[3, 4], [0, 0]] is
+    unchanged."""
     O2, v = oe.row_equalize(np.zeros((3, 5)), np.array([1.0, 2.0, 0.0]), 0.9, 1e-8)
     assert not O2.any()
     np.testing.assert_allclose(v, [0.9, 1.8, 0.0], rtol=1e-15)
+    O3, v3 = oe.row_equalize(np.array([[3.0, 4.0], [0.0, 0.0]]), np.zeros(2), 0.95, 0.0)
+    np.testing.assert_allclose(O3, [[3.0, 4.0], [0.0, 0.0]], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(v3, [0.625, 0.0], rtol=1e-14)
 
 
 ALL_PINS = [pin_e1_first_step_by_hand, pin_e2_later_step_by_hand,
