@@ -14,7 +14,8 @@ two staged gradient batches used alternately). Prints one JSON line:
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
   next_rows  the cautious-Adam step for the non-matrix parameters of the same model (the
              embedding-shaped set: 4 x 50257 x 768 bf16 + 64 scalars), timed on its own:
-             one launch per step, HBM bytes of the algorithm over the launch time
+             one launch per step, HBM bytes of the algorithm over the launch time; and the
+             same Muon step with the per-row energy equaliser switched on (its extra cost)
 
     python bench.py --adam-only     times only the cautious-Adam step (for profiling it)
 """
@@ -175,6 +176,43 @@ def bench_adam(steps, warmup, dev):
                          "bytes_per_launch": nbytes}}
 
 
+def bench_roweq(plan, W, G, M, wl, args, ms_plain):
+    """The same Muon step with the per-row energy equaliser on (fp32 row state, zero at the
+    start): step time, and the equaliser's own kernels (row sums of O^2 over the bf16 X, then
+    per-matrix factors) from the library's per-launch events."""
+    dev = W[0].device
+    V = [torch.zeros(s[0], dtype=torch.float32, device=dev) for s in wl.shapes]
+    cfg = make_config(row_equalize=True)
+    stream = torch.cuda.current_stream()
+    for t in range(args.warmup):
+        plan.step(W, G[t % 2], M, cfg, row_vars=V)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for t in range(args.steps):
+        plan.step(W, G[t % 2], M, cfg, row_vars=V)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    out = {"ms_per_step": ms, "steps_per_s": 1000.0 / ms, "ms_over_plain_step": ms - ms_plain,
+           "config": {"row_beta": cfg.row_beta, "row_eps": cfg.row_eps}}
+    if not args.no_profile:
+        plan.set_profiling(True)
+        for t in range(args.steps):
+            plan.step(W, G[t % 2], M, cfg, row_vars=V)
+        torch.cuda.synchronize()
+        kms, launches = plan.read_profile()["roweq"]
+        plan.set_profiling(False)
+        elems = wl.elements()
+        out["roweq_kernels_ms_per_step"] = kms / args.steps
+        out["roweq_launches_per_step"] = launches / args.steps
+        # algorithmic bytes: read O (bf16 X, 2 B/element) once for the row sums
+        out["rowsum_read_GBps"] = 2.0 * elems / (kms / args.steps * 1e-3) / 1e9
+    print(f"[bench] row equaliser: {ms:.4f} ms/step ({ms - ms_plain:+.4f})", file=sys.stderr,
+          flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +223,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
+    ap.add_argument("--no-roweq", action="store_true", help="skip the row-equaliser leg")
     ap.add_argument("--adam-only", action="store_true",
                     help="time only the cautious-Adam step and print its JSON object")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -293,11 +332,16 @@ def main():
                                "traffic": measured_traffic(dom, wl.name),
                                "avg_launch_us": 1e3 * dms / max(dl, 1)}
 
+    next_rows = {}
+    if not args.no_roweq:
+        next_rows["row_equalizer"] = bench_roweq(plan, W, G, M, wl, args, ms)
     plan.close()
     if not args.no_adam:
         del W, M, G
         torch.cuda.empty_cache()
-        out["next_rows"] = {"cautious_adam": bench_adam(args.steps, args.warmup, dev)}
+        next_rows["cautious_adam"] = bench_adam(args.steps, args.warmup, dev)
+    if next_rows:
+        out["next_rows"] = next_rows
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

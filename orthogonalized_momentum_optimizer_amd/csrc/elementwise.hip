@@ -191,18 +191,20 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* partials, int ti
 }
 
 // Row equaliser, pass 1: the sum of O^2 over each row of O in the caller's orientation,
-// O = X (or X^T for tall matrices) [* s1]; matrix q = blockIdx.y, rowsum[q * np + i].
+// O = X (or X^T for tall matrices) [* s1]; matrix q = blockIdx.y. Each slot owns
+// kRowParts x np floats of rowsum: partial sums, added in a fixed order by pass 2.
 // Wide matrices: one wavefront per row of X, 16-byte loads along the row (the padding
-// columns of X hold zeros, so vectors that cross cols read zeros). Tall matrices: a row of
-// O is a column of X; a block owns 256 columns, lane l of wave w sums columns 4l..4l+3 over
-// rows w, w+4, ... of X, and the four waves' partials are added in a fixed order.
+// columns of X hold zeros, so vectors that cross cols read zeros); one partial.
+// Tall matrices: a row of O is a column of X; a block owns 256 columns and one of
+// kRowParts slices of X's rows (blockIdx.z); lane l of wave w sums columns 4l..4l+3 over
+// rows w, w+4, ... of its slice, and the four waves' sums are added in a fixed order.
 template <int XDT>
 __global__ __launch_bounds__(256) void rowstat_kernel(ElemLaunch L) {
   __shared__ float part[4][256];
   const int q = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const void* x = static_cast<const char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
-  float* out = L.rowsum + (size_t)q * L.np;
+  float* out = L.rowsum + (size_t)q * kRowParts * L.np;
   const float s = L.apply_scale ? L.scales[4 * q] : 1.f;
   if (!L.tall) {
     const int i = blockIdx.x * 4 + w;
@@ -218,9 +220,11 @@ __global__ __launch_bounds__(256) void rowstat_kernel(ElemLaunch L) {
     return;
   }
   const int c0 = blockIdx.x * 256 + 4 * lane;
+  const int slice = (L.cols + kRowParts - 1) / kRowParts;
+  const int r_end = min(L.cols, (int)(blockIdx.z + 1) * slice);
   float a[4] = {0.f, 0.f, 0.f, 0.f};
   if (c0 < L.np) {
-    for (int r = w; r < L.cols; r += 4) {
+    for (int r = blockIdx.z * slice + w; r < r_end; r += 4) {
       float v[4];
       load4<XDT>(x, (size_t)r * L.np + c0, v);
 #pragma unroll
@@ -231,24 +235,28 @@ __global__ __launch_bounds__(256) void rowstat_kernel(ElemLaunch L) {
   for (int e = 0; e < 4; ++e) part[w][4 * lane + e] = a[e];
   __syncthreads();
   const int i = blockIdx.x * 256 + t;
-  if (i < L.rows) out[i] = ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) * (s * s);
+  if (i < L.rows)
+    out[(size_t)blockIdx.z * L.np + i] =
+        ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) * (s * s);
 }
 
 // Row equaliser, pass 2, one block per matrix q: v_i <- beta v_i + (1 - beta) rowsum_i / cols
 // (the caller's state, in place), d_i = 1 / (sqrt(v_i) + eps) (0 where that is 0: such a row
 // of O is zero), gamma = sqrt(sum_i rowsum_i / sum_i d_i^2 rowsum_i) in double and a fixed
 // order (0 when O is zero), rowf[q * np + i] = gamma d_i.
-__global__ __launch_bounds__(256) void roweq_finish_kernel(ElemLaunch L) {
-  __shared__ double red[2][4];
+__global__ __launch_bounds__(1024) void roweq_finish_kernel(ElemLaunch L) {
+  __shared__ double red[2][16];
   const int q = blockIdx.x, t = threadIdx.x;
-  const float* rs = L.rowsum + (size_t)q * L.np;
+  const float* rs = L.rowsum + (size_t)q * kRowParts * L.np;
+  const int parts = L.tall ? kRowParts : 1;
   float* f = L.rowf + (size_t)q * L.np;
   float* v = L.rowvar[q];
   const float inv_cols = 1.f / (float)L.cols;
   const float keep = 1.f - L.row_beta;
   double e = 0.0, e2 = 0.0;
-  for (int i = t; i < L.rows; i += 256) {
-    const float sum = rs[i];
+  for (int i = t; i < L.rows; i += 1024) {
+    float sum = rs[i];
+    for (int k = 1; k < parts; ++k) sum += rs[(size_t)k * L.np + i];
     const float vi = fmaf(L.row_beta, v[i], keep * (sum * inv_cols));
     v[i] = vi;
     const float den = sqrtf(vi) + L.row_eps;
@@ -264,10 +272,13 @@ __global__ __launch_bounds__(256) void roweq_finish_kernel(ElemLaunch L) {
     red[1][t >> 6] = e2;
   }
   __syncthreads();
-  const double te = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-  const double te2 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  double te = 0.0, te2 = 0.0;
+  for (int k = 0; k < 16; ++k) {
+    te += red[0][k];
+    te2 += red[1][k];
+  }
   const float gamma = te2 > 0.0 ? (float)sqrt(te / te2) : 0.f;
-  for (int i = t; i < L.rows; i += 256) f[i] *= gamma;
+  for (int i = t; i < L.rows; i += 1024) f[i] *= gamma;
 }
 
 // One 64x64 tile of the original orientation per block, matrix q = blockIdx.y:
@@ -356,14 +367,14 @@ hipError_t launch_norm(const float* partials, int tiles, float* scales, int coun
 
 hipError_t launch_rowstat(const ElemLaunch& L, int x_f32, hipStream_t s) {
   const int bx = L.tall ? (L.rows + 255) / 256 : (L.rows + 3) / 4;
-  const dim3 grid(bx, L.count), block(256);
+  const dim3 grid(bx, L.count, L.tall ? kRowParts : 1), block(256);
   if (x_f32) hipLaunchKernelGGL(rowstat_kernel<1>, grid, block, 0, s, L);
   else hipLaunchKernelGGL(rowstat_kernel<0>, grid, block, 0, s, L);
   return hipGetLastError();
 }
 
 hipError_t launch_roweq_finish(const ElemLaunch& L, hipStream_t s) {
-  hipLaunchKernelGGL(roweq_finish_kernel, dim3(L.count), dim3(256), 0, s, L);
+  hipLaunchKernelGGL(roweq_finish_kernel, dim3(L.count), dim3(1024), 0, s, L);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ int check_overlaps(std::vector<Range>& rs);
 constexpr int kPad = 128;        // wide shapes are padded to multiples of this
 constexpr int kTile = 64;        // elementwise kernels work on 64x64 tiles
 constexpr int kMaxPerLaunch = 48;  // matrices per elementwise launch (pointers travel by value)
+constexpr int kRowParts = 8;       // row equaliser: partial row sums per slot (tall matrices)
 
 // Elementwise launch over up to kMaxPerLaunch matrices of one shape and dtype pair.
 // Matrix q of the launch owns slot (slot0 + q) of its group's workspace buffers.
@@ -48,7 +49,8 @@ struct ElemLaunch {
   int apply_scale;                 // update: multiply X by s1 (ns_steps == 0)
   // row equaliser (per-slot arrays of np floats, slot0-based; nullptr = not used)
   float* rowvar[kMaxPerLaunch];    // finish: the caller's per-row state v
-  float* rowsum;                   // rowstat: out; finish: in (sums of O^2 per row)
+  float* rowsum;                   // rowstat: out; finish: in (kRowParts partial sums of O^2
+                                   // per row, np floats each, per slot)
   float* rowf;                     // finish: out; update: per-row factor of O
   float row_beta, row_eps;
 };

@@ -71,7 +71,7 @@ struct LaunchSet {  // matrices of one shape and dtype pair, contiguous slots of
 struct Group {
   int mp = 0, np = 0, count = 0, tiles64 = 0;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0, off_scales = 0;
-  size_t off_rowsum = 0, off_rowf = 0;  // row equaliser: count x np floats each
+  size_t off_rowsum = 0, off_rowf = 0;  // row equaliser: count x 8 x np and count x np floats
   std::vector<int> sets;
 };
 
@@ -279,7 +279,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
           E.x = xres + (size_t)slot * xslot;
           E.scales = scales + 4 * (size_t)slot;
           E.apply_scale = cfg->ns_steps == 0;
-          E.rowsum = rowsum + (size_t)slot * G.np;
+          E.rowsum = rowsum + (size_t)slot * kRowParts * G.np;
           E.rowf = rowf + (size_t)slot * G.np;
           E.row_beta = cfg->row_beta;
           E.row_eps = cfg->row_eps;
@@ -426,7 +426,7 @@ int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
     G.off_b = off; off = align256(off + as);
     G.off_part = off; off = align256(off + (size_t)G.count * G.tiles64 * 4);
     G.off_scales = off; off = align256(off + (size_t)G.count * 16);
-    G.off_rowsum = off; off = align256(off + (size_t)G.count * G.np * 4);
+    G.off_rowsum = off; off = align256(off + (size_t)G.count * kRowParts * G.np * 4);
     G.off_rowf = off; off = align256(off + (size_t)G.count * G.np * 4);
   }
   p->ws_bytes = off;
