@@ -28,6 +28,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Element index of (r, c) in the workspace matrix X (np columns): the tiled layout for
+// bf16, row-major for fp32. Four consecutive columns from a multiple of 4 stay contiguous.
+template <int XDT>
+__device__ __forceinline__ size_t xidx(int r, int c, int np) {
+  return XDT == 0 ? toff(r, c, np) : (size_t)r * np + c;
+}
+
 template <int DT>
 __device__ __forceinline__ float load1(const void* p, size_t i) {
   if (DT == 0) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
     }
     ss += (u[0] * u[0] + u[1] * u[1]) + (u[2] * u[2] + u[3] * u[3]);
     if (!L.tall) {
-      store4<XDT>(x, (size_t)r * L.np + c, u);  // wide (i, j) = (r, c); r < mp, c < np
+      store4<XDT>(x, xidx<XDT>(r, c, L.np), u);  // wide (i, j) = (r, c); r < mp, c < np
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[lr][lc + e] = u[e];
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = tile[b + e][a];
-      store4<XDT>(x, (size_t)(c0 + a) * L.np + (r0 + b), v);
+      store4<XDT>(x, xidx<XDT>(c0 + a, r0 + b, L.np), v);
     }
   }
 
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(256) void rowstat_kernel(ElemLaunch L) {
     float acc = 0.f;
     for (int c = 4 * lane; c < L.cols; c += 256) {
       float v[4];
-      load4<XDT>(x, (size_t)i * L.np + c, v);
+      load4<XDT>(x, xidx<XDT>(i, c, L.np), v);
       acc += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
     }
     acc = wave_sum(acc);
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void rowstat_kernel(ElemLaunch L) {
   if (c0 < L.np) {
     for (int r = blockIdx.z * slice + w; r < r_end; r += 4) {
       float v[4];
-      load4<XDT>(x, (size_t)r * L.np + c0, v);
+      load4<XDT>(x, xidx<XDT>(r, c0, L.np), v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = fmaf(v[e], v[e], a[e]);
     }
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(256) void update_kernel(ElemLaunch L) {
     for (int k = 0; k < 4; ++k) {
       const int a = (t >> 4) + 16 * k, b = 4 * (t & 15);
       float v[4];
-      load4<XDT>(x, (size_t)(c0 + a) * L.np + (r0 + b), v);  // within the padded buffer
+      load4<XDT>(x, xidx<XDT>(c0 + a, r0 + b, L.np), v);  // within the padded buffer
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[a][b + e] = v[e];
     }
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(256) void update_kernel(ElemLaunch L) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) ov[e] = tile[lc + e][lr_];
     } else {
-      load4<XDT>(x, (size_t)r * L.np + c, ov);
+      load4<XDT>(x, xidx<XDT>(r, c, L.np), ov);
     }
     const float sr = rowf ? s * rowf[r] : s;
 #pragma unroll

@@ -1,4 +1,7 @@
 // Internal interfaces between the host plan (plan.hip) and the kernel launchers.
+//
+// Workspace matrices in bf16 (the bf16 rounds) use the tiled layout of toff(); in fp32 (the
+// debug rounds) they are plain row-major.
 // Every launcher enqueues on `stream`, returns the hipError_t of the launch, and assumes the
 // host has validated shapes, pointers and the workspace layout.
 #pragma once
@@ -24,6 +27,16 @@ struct Range {
 int check_overlaps(std::vector<Range>& rs);
 
 constexpr int kPad = 128;        // wide shapes are padded to multiples of this
+
+// Layout of the bf16 workspace matrices (X, A, B'; C columns, C a multiple of 32, rows a
+// multiple of 16): 16 x 32 tiles of 1 KB, row-major inside a tile, tiles in row-major order.
+// A 16-row by 32-column block, which one direct-to-LDS load instruction of the product
+// kernels fetches, is then one contiguous kilobyte, and a 32-column step of K is +1 KB.
+__host__ __device__ __forceinline__ size_t toff(int r, int c, int C) {
+  return ((size_t)(r >> 4) * (size_t)(C >> 5) + (size_t)(c >> 5)) * 512u +
+         (size_t)((r & 15) << 5) + (size_t)(c & 31);
+}
+constexpr int kTileBytes = 1024;  // one 16 x 32 bf16 tile
 constexpr int kTile = 64;        // elementwise kernels work on 64x64 tiles
 constexpr int kMaxPerLaunch = 48;  // matrices per elementwise launch (pointers travel by value)
 constexpr int kRowParts = 8;       // row equaliser: partial row sums per slot (tall matrices)

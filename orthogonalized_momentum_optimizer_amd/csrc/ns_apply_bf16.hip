@@ -119,20 +119,20 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
       const int row = 16 * (4 * wave + op) + (lane >> 2);
       const int ch = (lane & 3) ^ kswz(row);
       const uint32_t grow = min(c.row0 + row, g.mp - 1);
-      c.doff[op] = 2u * (grow * (uint32_t)g.mp + 8u * ch);
+      c.doff[op] = 2u * (uint32_t)toff((int)grow, 8 * ch, g.mp);
     }
 #pragma unroll
     for (int op = 0; op < 4; ++op) {
       const int kk = 2 * (4 * wave + op) + (lane >> 5);
       const int ch = (lane & 31) ^ (2 * (kk & 3));
       const uint32_t gcol = min(c.col0 + 8 * ch, g.np - 8);
-      c.doff[4 + op] = 2u * ((uint32_t)kk * (uint32_t)g.np + gcol);
+      c.doff[4 + op] = 2u * (uint32_t)toff(kk, (int)gcol, g.np);
     }
   };
   auto dma_op = [&](const Tile& c, int kt, int op) {
     u32x4* st = smem + (kt & (NSTAGE - 1)) * kUnitsStage;
     if (op < 4)
-      __builtin_amdgcn_global_load_lds(c.lhs + (size_t)kt * (2 * TK) + c.doff[op],
+      __builtin_amdgcn_global_load_lds(c.lhs + (size_t)kt * kTileBytes + c.doff[op],
                                        MUON_LDS_PTR(st + 64 * (4 * wave + op)), 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(c.rhs + (size_t)kt * rhs_stage_bytes + c.doff[op],
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
         const int cr = (t >> 5) + 8 * k;
         const int grow = row0 + 32 * i + (cr & 31) + 128 * (cr >> 5), gcol = col0 + 8 * ch;
         if (grow < g.mp && gcol < g.np)
-          *reinterpret_cast<u32x4*>(out + (size_t)grow * g.np + gcol) = w[k];
+          *reinterpret_cast<u32x4*>(out + toff(grow, gcol, g.np)) = w[k];
       }
     }
   }

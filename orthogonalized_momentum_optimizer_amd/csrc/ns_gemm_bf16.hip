@@ -21,8 +21,9 @@
 // Tiling: 256 threads (4 waves as 2x2), a 128x128 output tile per block, each wave 64x64
 // (2x2 blocks of v_mfma_f32_32x32x16_bf16). K advances 32 at a time through a ring of 4 LDS
 // stages of 16 KB (64 KB per block, two blocks per CU), filled with direct-to-LDS loads three
-// stages ahead. Both operands are K-contiguous (rows of X, rows of A; layouts in
-// mfma_common.h).
+// stages ahead. Both operands are K-contiguous (rows of X, rows of A); X, A and B' are stored
+// in the 16 x 32 tiled layout (toff), so each load instruction (16 rows x 32 columns) reads
+// one contiguous kilobyte.
 #include <vector>
 
 #include "mfma_common.h"
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
     const int row = 16 * (2 * wave + (op & 1)) + (lane >> 2);
     const int c = (lane & 3) ^ kswz(row);
     const uint32_t grow = min((op < 2 ? I * BM : J * BN) + row, g.mp - 1);
-    doff[op] = 2u * (grow * (uint32_t)g.ld_in + 8u * c);
+    doff[op] = 2u * (uint32_t)toff((int)grow, 8 * c, g.ld_in);
   }
   // A diagonal tile (I == J) multiplies a row block by itself: it loads the block once and
   // reads both operands from it (half the stage traffic of an off-diagonal tile).
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
     constexpr int kLoads = kDiag ? 2 : kLoadsPerStage;  // direct loads per wave per stage
     auto issue = [&](int kt) {
       u32x4* st = smem + (kt & (STAGES - 1)) * kStage;
-      const char* base = srcb + (size_t)kt * (2 * BK);
+      const char* base = srcb + (size_t)kt * kTileBytes;  // next 32-column tile
 #pragma unroll
       for (int op = 0; op < kLoads; ++op)
         __builtin_amdgcn_global_load_lds(base + doff[op],
@@ -244,8 +245,7 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
         if (diag && 8 * ch + e == row) v[e] += g.a;
       }
     }
-    *reinterpret_cast<u32x4*>(out + (size_t)(I * BM + row) * ld + J * BN + 8 * ch) =
-        pack_bf16x8(v);
+    *reinterpret_cast<u32x4*>(out + toff(I * BM + row, J * BN + 8 * ch, ld)) = pack_bf16x8(v);
     if (!diag) {
       *reinterpret_cast<f32x4*>(st + stage_idx(row, 8 * ch)) = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4*>(st + stage_idx(row, 8 * ch + 4)) = f32x4{v[4], v[5], v[6], v[7]};
@@ -261,8 +261,7 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = st[stage_idx(8 * ch + e, col)];
-      *reinterpret_cast<u32x4*>(out + (size_t)(J * BN + col) * ld + I * BM + 8 * ch) =
-          pack_bf16x8(v);
+      *reinterpret_cast<u32x4*>(out + toff(J * BN + col, I * BM + 8 * ch, ld)) = pack_bf16x8(v);
     }
   }
 }

@@ -120,11 +120,11 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Launch S) {
     const int row = 16 * (4 * wave + (op & 3)) + (lane >> 2);
     const int c = (lane & 3) ^ kswz(row);
     const uint32_t grow = min((op < 4 ? row0 : col0) + row, g.mp - 1);
-    doff[op] = 2u * (grow * (uint32_t)g.ld_in + 8u * c);
+    doff[op] = 2u * (uint32_t)toff((int)grow, 8 * c, g.ld_in);
   }
   auto dma_op = [&](int kt, int op) {
     u32x4* st = smem + (kt & (NSTAGE - 1)) * kUnitsStage + (op >> 2) * kUnitsHalf;
-    __builtin_amdgcn_global_load_lds(src + (size_t)kt * (2 * TK) + doff[op],
+    __builtin_amdgcn_global_load_lds(src + (size_t)kt * kTileBytes + doff[op],
                                      MUON_LDS_PTR(st + 64 * (4 * wave + (op & 3))), 16, 0, 0);
   };
 
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Launch S) {
     const int r = 64 * part + 2 * blk + (lane >> 5);
     const int gch = (lane & 31) ^ (r & 31);
     const uint32_t grow = min(row0 + r, g.mp - 1), gcol = min(col0 + 8 * gch, g.mp - 8);
-    __builtin_amdgcn_global_load_lds(src + 2 * ((size_t)grow * g.mp + gcol),
+    __builtin_amdgcn_global_load_lds(src + 2 * toff((int)grow, (int)gcol, g.mp),
                                      MUON_LDS_PTR(smem + part * kUnitsStage + 64 * blk), 16, 0,
                                      0);
   };
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Launch S) {
       for (int u = 0; u < 8; ++u) {
         const int r = (t >> 5) + 8 * (kb + u);
         if (row0 + r < mp && col0 + 8 * ch < mp && (!diag || 8 * ch >= r))
-          *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * mp + col0 + 8 * ch) = w[u];
+          *reinterpret_cast<u32x4*>(out + toff(row0 + r, col0 + 8 * ch, mp)) = w[u];
       }
     }
   }
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void ns_sym256_bf16(Sym256Launch S) {
             w[e] = (w[e] & keep) | (rowv[u][e] & ~keep);
           }
         }
-        *reinterpret_cast<u32x4*>(out + (size_t)(col0 + R) * mp + row0 + r0) = w;
+        *reinterpret_cast<u32x4*>(out + toff(col0 + R, row0 + r0, mp)) = w;
       }
     }
   }
