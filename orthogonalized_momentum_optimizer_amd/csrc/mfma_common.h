@@ -2,7 +2,8 @@
 //
 // Operand tiles move global -> LDS with 16-byte direct-to-LDS loads (global_load_lds):
 // a wave instruction fills 1 KB of LDS linearly (lane l at byte 16 l), so the XOR swizzles
-// below are applied by choosing which global 16-byte chunk each lane fetches.
+// below are applied by choosing which global 16-byte chunk each lane fetches. In global
+// memory the bf16 matrices use the 16 x 32 tiled layout of toff() (muon_internal.h).
 //
 //  - K-contiguous tiles: ROWS rows x 32 K-values (4 chunks of 16 bytes per row); chunk c of
 //    row r is stored at c ^ ((r >> 2) & 3). A fragment read (16 consecutive lanes = 16
@@ -95,73 +96,16 @@ __device__ __forceinline__ void vm_wait() {
 
 __device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
 
-// K-contiguous ROWS x 32 tile (rows row0.. of `src`, K from k0) into `stage` (16-byte units at
-// row*4 + chunk). Rows at or beyond `row_end` are fetched from row_end - 1 instead (their
-// products are never stored). With NW waves each wave issues ROWS/(16 NW) 1 KB blocks.
-template <int ROWS, int NW>
-__device__ __forceinline__ void dma_kmajor(const uint16_t* src, int ld, int row0, int row_end,
-                                           int k0, u32x4* stage) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int kPerWave = ROWS / 16 / NW;
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int blk = kPerWave * w + i;
-    const int row = 16 * blk + (lane >> 2);
-    const int c = (lane & 3) ^ kswz(row);
-    const int grow = min(row0 + row, row_end - 1);
-    __builtin_amdgcn_global_load_lds(src + (size_t)grow * ld + k0 + 8 * c,
-                                     MUON_LDS_PTR(stage + 64 * blk), 16, 0, 0);
-  }
-}
-
-// N-contiguous 32(k) x COLS(n) tile (K-rows k0.. of `src`, columns col0..) into `stage`
-// (units at k*(COLS/8) + chunk). Columns at or beyond `col_end` (a multiple of 8) are fetched
-// from the last valid chunk instead.
-template <int COLS, int NW>
-__device__ __forceinline__ void dma_nmajor(const uint16_t* src, int ld, int k0, int col0,
-                                           int col_end, u32x4* stage) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int kChunks = COLS / 8, kRowsPerBlk = 64 / kChunks;
-  constexpr int kPerWave = 32 / kRowsPerBlk / NW;
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int blk = kPerWave * w + i;
-    const int k = kRowsPerBlk * blk + lane / kChunks;
-    const int c = (lane % kChunks) ^ (2 * (k & 3));
-    const int gcol = min(col0 + 8 * c, col_end - 8);
-    __builtin_amdgcn_global_load_lds(src + (size_t)(k0 + k) * ld + gcol,
-                                     MUON_LDS_PTR(stage + 64 * blk), 16, 0, 0);
-  }
-}
-
 // One K-contiguous fragment: 8 K-values (chunk c) of LDS row `row`.
 __device__ __forceinline__ bf16x8 frag_k(const u32x4* stage, int row, int c) {
   return __builtin_bit_cast(bf16x8, stage[row * 4 + (c ^ kswz(row))]);
 }
 
-// ds_read_b64_tr_b16 issued as inline assembly: through the builtin, the compiler waits for
-// every outstanding direct-to-LDS load (vmcnt 0) before the read, which would drain the load
-// pipeline each step. The result is valid only after lds_wait().
-__device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
-  const unsigned addr = static_cast<unsigned>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-  s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-
-// 16-byte LDS read issued as inline assembly (see ds_read_tr): valid only after an explicit
-// lgkmcnt wait that names the result.
-__device__ __forceinline__ u32x4 ds_read_b128(const u32x4* p) {
-  const unsigned addr = static_cast<unsigned>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-
-// The same reads from a byte address in LDS plus a compile-time offset (the instruction's
-// 16-bit offset field), so that a run of reads shares one address register.
+// ds_read_b64_tr_b16 and ds_read_b128 issued as inline assembly, from a byte address in LDS
+// plus a compile-time offset (the instruction's 16-bit offset field, so that a run of reads
+// shares one address register). Through the builtins the compiler waits for every
+// outstanding direct-to-LDS load (vmcnt 0) before the read, which would drain the load
+// pipeline; these results are valid only after an explicit lgkmcnt wait that names them.
 template <int OFF>
 __device__ __forceinline__ s16x4 ds_read_tr_at(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
@@ -200,29 +144,6 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Waits for this wave's LDS reads; ties the fragments to the wait so no use moves above it.
-__device__ __forceinline__ void lds_wait(bf16x8& x, bf16x8& y) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y));
-}
-
-// One transposed fragment of an N-contiguous tile with COLS columns: lane l gets K-values
-// kb + 8(l/32) + 0..7 of column nb + l%32 (valid after lds_wait).
-template <int COLS>
-__device__ __forceinline__ bf16x8 frag_n(const u32x4* stage, int kb, int nb, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int n = nb + 16 * (g & 1) + 4 * (j & 3);
-  const uint16_t* base = reinterpret_cast<const uint16_t*>(stage);
-  s16x4 h[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int k = kb + 8 * (g >> 1) + 4 * half + (j >> 2);
-    const int c = (n >> 3) ^ (2 * (k & 3));
-    h[half] = ds_read_tr(base + k * COLS + 8 * c + (n & 7));
-  }
-  const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 }  // namespace mfma
