@@ -399,3 +399,23 @@ def test_adam_validation_passes_for_legal_sets():
         e.append([0, 0, 0, 0, 0, 0, 0, 1.0])
     status, msg = _adam_fake_call(mutate)
     assert status == L.MUON_ERR_HIP, msg
+
+
+# ---- randomized plans: grouping and workspace size against a model of the layout -----------
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(1, 3000), st.integers(1, 3000),
+                          st.sampled_from([0, 1]), st.sampled_from([0, 1])),
+                min_size=1, max_size=12),
+       st.sampled_from([(L.MUON_NS_BF16, 2), (L.MUON_NS_F32_DEBUG, 4)]))
+def test_random_plans_workspace_model(mats, prec_esz):
+    prec, esz = prec_esz
+    rows, cols = [m[0] for m in mats], [m[1] for m in mats]
+    p = L.muon_plan_create(rows, cols, [m[2] for m in mats], [m[3] for m in mats], prec)
+    try:
+        assert L.muon_plan_workspace_size(p) == _ws_expected(list(zip(rows, cols)), esz)
+    finally:
+        L.muon_plan_destroy(p)
