@@ -93,16 +93,18 @@ struct NsGroup {
 };
 // bf16 storage, bf16 matrix cores with fp32 accumulation. The bf16 round folds a I into B:
 // poly writes B' = aI + bA + cAA and apply forms s1 B' X. Each launcher takes one or more
-// shape groups of a round (the step passes one group at a time). Gram and poly: groups with
-// use_sym256 (mp >= 1024) share 256x256-tile launches (one per 8 groups, tiles ordered
-// longest first on every XCD; ns_sym256_bf16.hip), smaller groups use 128x128 tiles, one
-// launch each (ns_gemm_bf16.hip). Apply: 256x256 tiles, one launch per group
+// shape groups of a round (the step passes one group at a time, or all of them when they are
+// too small to fill the device one by one). Gram and poly: groups with use_sym256
+// (mp >= 1024) share 256x256-tile launches (ns_sym256_bf16.hip), smaller groups 128x128-tile
+// launches (ns_gemm_bf16.hip); up to 8 groups per launch, tiles ordered longest first on
+// every XCD. Apply: 256x256 tiles, groups of equal mp in one persistent launch
 // (ns_apply_bf16.hip).
 bool use_sym256(const NsGroup& g);
 hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s);   // A = s2 X X^T
 hipError_t launch_poly_bf16(const NsGroup* groups, int n, float a, float b, float c,
                             hipStream_t s);                                 // B' = aI+bA+cAA
 hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s);  // X' = s1 B' X
+int device_cus();  // compute units of the current device
 hipError_t launch_gram256_bf16(const NsGroup* groups, int n, hipStream_t s);
 hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, float c,
                                hipStream_t s);

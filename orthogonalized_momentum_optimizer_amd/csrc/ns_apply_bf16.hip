@@ -24,6 +24,7 @@
 // transposed product: element r of lane l is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4],
 // so each register quad is 4 consecutive columns of one row: one 8-byte store.
 #include <algorithm>
+#include <vector>
 
 #include "mfma_common.h"
 
@@ -37,13 +38,18 @@ constexpr int kUnitsA = TM * TK / 8;           // 1024 16-byte units
 constexpr int kUnitsStage = kUnitsA + TK * TN / 8;
 constexpr int kLoadsPerStage = (TM / 16) / 4 + (32 / 2) / 4;  // per wave: 4 + 4
 
-struct ApplyArgs {      // one shape group
+struct ApplyGroup {     // one shape group
   const uint16_t* b;   // B', batch x mp x mp
   const uint16_t* x;   // X, batch x mp x np
   uint16_t* out;       // X', batch x mp x np
   const float* scales; // per matrix {s1, s2, nu, 0}, or null (scale 1)
-  int mp, np;
-  int tiles_m, tiles_n, total_tiles;
+  int np, tiles_n, per_mat;
+  int first;           // the group's first tile in the launch's tile order
+};
+
+struct ApplyArgs {      // the shape groups of one launch, all of one mp
+  ApplyGroup g[kMaxLaunchGroups];
+  int n, mp, tiles_m, total_tiles;
 };
 
 // Fragments of one 16-wide K slice: 8 transposed half-fragments of the right operand and 4
@@ -68,10 +74,20 @@ __device__ __forceinline__ void lds_op(uint32_t va, uint32_t vb, Frags& f) {
   }
 }
 
+// The launch's arguments in the kernel-argument segment (constant memory): an element picked
+// with a run-time index is read with a scalar load instead of copying the whole table.
+template <typename T>
+__device__ __forceinline__ const T* kernel_args() {
+  return (const T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 // Output staging of the epilogue: 64 rows x 256 columns of bf16 (32 KB) beside the ring.
 constexpr int kUnitsOut = 64 * TN / 8;
 
-__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
+// The kernel body. kMulti: the launch holds several groups (tile -> group lookup); a single
+// group's tiles skip the lookup and the dependent argument load it needs.
+template <bool kMulti>
+__device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
   __shared__ u32x4 smem[NSTAGE * kUnitsStage + kUnitsOut];  // 128 KB ring + 32 KB staging
 
   const int t = threadIdx.x;
@@ -85,19 +101,20 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   // contiguous range [lo, hi) of the group's tiles (nb = the XCD's block count), so the CUs
   // of one XCD work on neighbouring tiles of the same matrices at the same time.
   const int x = blockIdx.x & 7, k0 = blockIdx.x >> 3;
-  const int T = g.total_tiles, G = gridDim.x;
+  const int T = g.total_tiles, G = gridDim.x;  // tiles of all groups, in group order
   const int lo = xcd_remap(x, T);  // first tile of XCD x
   const int nt = T / 8 + (x < (T & 7) ? 1 : 0);
   const int nb = G / 8 + (x < (G & 7) ? 1 : 0);
-  const int per_mat = g.tiles_m * g.tiles_n;
-  const size_t mm = (size_t)g.mp * g.mp, mn = (size_t)g.mp * g.np;
-  const size_t rhs_stage_bytes = (size_t)2 * TK * g.np;
+  const size_t mm = (size_t)g.mp * g.mp;
   const int KT = g.mp / TK;
 
   struct Tile {
-    int bidx, row0, col0;
+    int bidx, row0, col0, np;
     const char* lhs;
     const char* rhs;
+    size_t rhs_stage_bytes;  // one 32-row K step of X
+    uint16_t* out;           // the matrix's X'
+    const float* scale;      // the matrix's scale record, or null
     uint32_t doff[8];
   };
   // Direct-to-LDS loads, 8 per wave per stage, one instruction each: loads 0-3 fetch 16
@@ -107,13 +124,29 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
   // wave-uniform base (the operand's stage origin, in scalar registers) plus the lane's
   // 32-bit byte offset, fixed for the tile.
   auto setup = [&](int L, Tile& c) {
-    c.bidx = L / per_mat;
-    const int tt = L - c.bidx * per_mat;
-    const int I = tt / g.tiles_n, J = tt - (tt / g.tiles_n) * g.tiles_n;
+    // the tile's group: the last one whose first tile is at or below L; its record is
+    // read from the kernel-argument segment (scalar loads), so only the chosen group's
+    // fields occupy registers
+    int k = 0;
+    if constexpr (kMulti) {
+#pragma unroll
+      for (int j = 1; j < kMaxLaunchGroups; ++j)
+        if (j < g.n && L >= g.g[j].first) k = j;
+    }
+    const ApplyGroup& q = kMulti ? kernel_args<ApplyArgs>()->g[k] : g.g[0];
+    const int l = L - q.first;
+    c.bidx = l / q.per_mat;
+    const int tt = l - c.bidx * q.per_mat;
+    const int I = tt / q.tiles_n, J = tt - (tt / q.tiles_n) * q.tiles_n;
+    const size_t mn = (size_t)g.mp * q.np;
     c.row0 = I * TM;
     c.col0 = J * TN;
-    c.lhs = reinterpret_cast<const char*>(g.b + c.bidx * mm);
-    c.rhs = reinterpret_cast<const char*>(g.x + c.bidx * mn);
+    c.np = q.np;
+    c.lhs = reinterpret_cast<const char*>(q.b + c.bidx * mm);
+    c.rhs = reinterpret_cast<const char*>(q.x + c.bidx * mn);
+    c.rhs_stage_bytes = (size_t)2 * TK * q.np;
+    c.out = q.out + c.bidx * mn;
+    c.scale = q.scales ? q.scales + 4 * c.bidx : nullptr;
 #pragma unroll
     for (int op = 0; op < 4; ++op) {
       const int row = 16 * (4 * wave + op) + (lane >> 2);
@@ -125,8 +158,8 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     for (int op = 0; op < 4; ++op) {
       const int kk = 2 * (4 * wave + op) + (lane >> 5);
       const int ch = (lane & 31) ^ (2 * (kk & 3));
-      const uint32_t gcol = min(c.col0 + 8 * ch, g.np - 8);
-      c.doff[4 + op] = 2u * (uint32_t)toff(kk, (int)gcol, g.np);
+      const uint32_t gcol = min(c.col0 + 8 * ch, c.np - 8);
+      c.doff[4 + op] = 2u * (uint32_t)toff(kk, (int)gcol, c.np);
     }
   };
   auto dma_op = [&](const Tile& c, int kt, int op) {
@@ -135,7 +168,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
       __builtin_amdgcn_global_load_lds(c.lhs + (size_t)kt * kTileBytes + c.doff[op],
                                        MUON_LDS_PTR(st + 64 * (4 * wave + op)), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(c.rhs + (size_t)kt * rhs_stage_bytes + c.doff[op],
+      __builtin_amdgcn_global_load_lds(c.rhs + (size_t)kt * c.rhs_stage_bytes + c.doff[op],
                                        MUON_LDS_PTR(st + kUnitsA + 64 * (4 * wave + op - 4)),
                                        16, 0, 0);
   };
@@ -266,7 +299,9 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     // output drains through the staging area
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int bidx = cur.bidx, row0 = cur.row0, col0 = cur.col0;
+    const int row0 = cur.row0, col0 = cur.col0, np = cur.np;
+    uint16_t* const out = cur.out;
+    const float* const scale = cur.scale;
     if (L + nb < hi) {
       setup(L + nb, cur);
 #pragma unroll
@@ -278,8 +313,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
     // the scale is 1 after the first round: skip its multiplies there. Every LDS access
     // below is inline assembly and the scale a scalar load, so nothing here waits for the
     // next tile's loads.
-    const float s = g.scales ? scalar_load_f32(g.scales + 4 * bidx) : 1.f;
-    uint16_t* out = g.out + bidx * mn;
+    const float s = scale ? scalar_load_f32(scale) : 1.f;
     const uint32_t stb = lds0 + 16u * (NSTAGE * kUnitsStage);  // staging base, bytes
     auto stage_chunk = [&](int i, auto scaled_t) {
       constexpr bool scaled = decltype(scaled_t)::value;
@@ -307,7 +341,7 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i > 0) lds_barrier();  // the previous chunk has been read out
-      if (g.scales) stage_chunk(i, std::true_type{});
+      if (scale) stage_chunk(i, std::true_type{});
       else stage_chunk(i, std::false_type{});
       lds_barrier();
       u32x4 w[8];
@@ -323,11 +357,23 @@ __global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
       for (int k = 0; k < 8; ++k) {
         const int cr = (t >> 5) + 8 * k;
         const int grow = row0 + 32 * i + (cr & 31) + 128 * (cr >> 5), gcol = col0 + 8 * ch;
-        if (grow < g.mp && gcol < g.np)
-          *reinterpret_cast<u32x4*>(out + toff(grow, gcol, g.np)) = w[k];
+        if (grow < g.mp && gcol < np)
+          *reinterpret_cast<u32x4*>(out + toff(grow, gcol, np)) = w[k];
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) { apply_tiles<false>(g); }
+
+__global__ __launch_bounds__(256) void ns_apply_bf16_groups(ApplyArgs g) {
+  apply_tiles<true>(g);
+}
+
+// launches the grid for a single group or for several
+void launch_apply_grid(const ApplyArgs& a, dim3 grid, hipStream_t s) {
+  if (a.n > 1) hipLaunchKernelGGL(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(ns_apply_bf16, grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -344,23 +390,32 @@ int device_cus() {
   return n;
 }
 
-// One launch per group: a grid over several groups (each XCD taking its share of each) was
-// measured no faster for this kernel, whose tiles all cost the same for a given mp.
+// All groups of a call with the same mp in one persistent grid (their tiles all cost the
+// same: K = mp). A step calls with one group at a time unless its groups are too small to
+// fill the device on their own.
 hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
-  for (int k = 0; k < n; ++k) {
-    const NsGroup& G = groups[k];
+  std::vector<bool> done(n, false);
+  for (int k0 = 0; k0 < n; ++k0) {
+    if (done[k0]) continue;
     ApplyArgs a{};
-    a.b = static_cast<const uint16_t*>(G.b);
-    a.x = static_cast<const uint16_t*>(G.x_in);
-    a.out = static_cast<uint16_t*>(G.x_out);
-    a.scales = G.first ? G.scales : nullptr;
-    a.mp = G.mp;
-    a.np = G.np;
-    a.tiles_m = (G.mp + TM - 1) / TM;
-    a.tiles_n = (G.np + TN - 1) / TN;
-    a.total_tiles = a.tiles_m * a.tiles_n * G.batch;
-    hipLaunchKernelGGL(ns_apply_bf16, dim3(std::min(a.total_tiles, device_cus())), dim3(256), 0,
-                       s, a);
+    a.mp = groups[k0].mp;
+    a.tiles_m = (a.mp + TM - 1) / TM;
+    for (int k = k0; k < n && a.n < kMaxLaunchGroups; ++k) {
+      const NsGroup& G = groups[k];
+      if (done[k] || G.mp != a.mp) continue;
+      done[k] = true;
+      ApplyGroup& q = a.g[a.n++];
+      q.b = static_cast<const uint16_t*>(G.b);
+      q.x = static_cast<const uint16_t*>(G.x_in);
+      q.out = static_cast<uint16_t*>(G.x_out);
+      q.scales = G.first ? G.scales : nullptr;
+      q.np = G.np;
+      q.tiles_n = (G.np + TN - 1) / TN;
+      q.per_mat = a.tiles_m * q.tiles_n;
+      q.first = a.total_tiles;
+      a.total_tiles += q.per_mat * G.batch;
+    }
+    launch_apply_grid(a, dim3(std::min(a.total_tiles, device_cus())), s);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

@@ -24,6 +24,7 @@
 // stages ahead. Both operands are K-contiguous (rows of X, rows of A); X, A and B' are stored
 // in the 16 x 32 tiled layout (toff), so each load instruction (16 rows x 32 columns) reads
 // one contiguous kilobyte.
+#include <algorithm>
 #include <vector>
 
 #include "mfma_common.h"
@@ -39,14 +40,19 @@ constexpr int kLoadsPerStage = 4;  // direct-to-LDS loads per wave per stage
 
 enum Mode { GRAM = 0, POLY = 1 };
 
-struct SymArgs {
+struct SymArgs {         // one shape group
   const uint16_t* in;   // GRAM: X (batch x mp x np); POLY: A (batch x mp x mp)
   uint16_t* out;        // batch x mp x mp
+  const float* scales;  // GRAM first round: per matrix {s1, s2, nu, 0}; else null
   long long in_bs;
   int ld_in, K;
   int mp, tiles;        // tiles per side (mp / 128)
-  int tiles_per_mat, total_tiles;
-  const float* scales;  // GRAM first round: per matrix {s1, s2, nu, 0}; else null
+  int tiles_per_mat;
+};
+
+struct SymLaunch {      // the shape groups of one launch, longest tiles (largest K) first
+  TileSplit split;
+  SymArgs g[kMaxLaunchGroups];
   float a, b, c;        // POLY coefficients
 };
 
@@ -67,8 +73,10 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float v[8]) {
   return o;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
+// kMulti: the launch holds several groups (block -> group lookup); a single group's blocks
+// skip the lookup and the dependent argument load it needs.
+template <int MODE, bool kMulti>
+__global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
   // STAGES ring buffers; stage s holds the left tile at units [1024 s, 1024 s + 512) and the
   // right tile at [1024 s + 512, 1024 (s + 1)). The epilogue reuses all 64 KB.
   __shared__ u32x4 smem[STAGES * kStage];
@@ -79,7 +87,14 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
-  const int L = xcd_remap(blockIdx.x, g.total_tiles);
+  int L = 0;
+  SymArgs g;
+  if constexpr (kMulti) {
+    g = S.g[split_block(blockIdx.x, S.split, L)];
+  } else {
+    g = S.g[0];
+    L = xcd_remap(blockIdx.x, gridDim.x);
+  }
   const int bidx = L / g.tiles_per_mat;
   int tt = L - bidx * g.tiles_per_mat;
   int I = 0;
@@ -241,8 +256,8 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
       } else {
         const uint32_t w = epre[k][e >> 1];
         const float x = bf2f((e & 1) ? (w >> 16) : (w & 0xffffu));
-        v[e] = fmaf(g.b, x, g.c * a[e]);
-        if (diag && 8 * ch + e == row) v[e] += g.a;
+        v[e] = fmaf(S.b, x, S.c * a[e]);
+        if (diag && 8 * ch + e == row) v[e] += S.a;
       }
     }
     *reinterpret_cast<u32x4*>(out + toff(I * BM + row, J * BN + 8 * ch, ld)) = pack_bf16x8(v);
@@ -266,67 +281,86 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymArgs g) {
   }
 }
 
-SymArgs sym_args(const NsGroup& G) {
-  SymArgs a{};
-  a.mp = G.mp;
-  a.tiles = G.mp / BM;
-  a.tiles_per_mat = a.tiles * (a.tiles + 1) / 2;
-  a.total_tiles = a.tiles_per_mat * G.batch;
-  return a;
-}
-
-}  // namespace
-
-namespace {
-
-hipError_t launch_gram128(const NsGroup& G, hipStream_t s) {
-  SymArgs a = sym_args(G);
-  a.in = static_cast<const uint16_t*>(G.x_in);
-  a.out = static_cast<uint16_t*>(G.a);
-  a.in_bs = (long long)G.mp * G.np;
-  a.ld_in = G.np;
-  a.K = G.np;
-  a.scales = G.first ? G.scales : nullptr;
-  hipLaunchKernelGGL(ns_sym_bf16<GRAM>, dim3(a.total_tiles), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_poly128(const NsGroup& G, float ca, float cb, float cc, hipStream_t s) {
-  SymArgs a = sym_args(G);
-  a.in = static_cast<const uint16_t*>(G.a);
-  a.out = static_cast<uint16_t*>(G.b);
-  a.in_bs = (long long)G.mp * G.mp;
-  a.ld_in = G.mp;
-  a.K = G.mp;
-  a.a = ca;
-  a.b = cb;
-  a.c = cc;
-  hipLaunchKernelGGL(ns_sym_bf16<POLY>, dim3(a.total_tiles), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 // Groups with use_sym256 go to the 256-tile kernel together (ns_sym256_bf16.hip); the rest
-// run here, one launch per group.
-hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s) {
+// run here, all groups of a call in one grid (a step calls with one group at a time unless
+// its groups are too small to fill the device on their own).
+namespace {
+
+hipError_t launch_sym128(const NsGroup* const* groups, int n, int mode, float ca, float cb,
+                         float cc, hipStream_t s) {
+  // per-tile work is the K loop: np for GRAM, mp for POLY
+  auto K = [&](const NsGroup* G) { return mode == GRAM ? G->np : G->mp; };
+  std::vector<const NsGroup*> order(groups, groups + n);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](const NsGroup* x, const NsGroup* y) { return K(x) > K(y); });
+  for (int c0 = 0; c0 < n; c0 += kMaxLaunchGroups) {
+    SymLaunch a{};
+    a.a = ca;
+    a.b = cb;
+    a.c = cc;
+    int total = 0, left = 0;
+    a.split.n = std::min(kMaxLaunchGroups, n - c0);
+    for (int k = 0; k < a.split.n; ++k) {
+      const NsGroup& G = *order[c0 + k];
+      SymArgs& g = a.g[k];
+      g.in = static_cast<const uint16_t*>(mode == GRAM ? G.x_in : G.a);
+      g.out = static_cast<uint16_t*>(mode == GRAM ? G.a : G.b);
+      g.scales = (mode == GRAM && G.first) ? G.scales : nullptr;
+      g.in_bs = mode == GRAM ? (long long)G.mp * G.np : (long long)G.mp * G.mp;
+      g.ld_in = K(&G);
+      g.K = K(&G);
+      g.mp = G.mp;
+      g.tiles = G.mp / BM;
+      g.tiles_per_mat = g.tiles * (g.tiles + 1) / 2;
+      const int tiles = g.tiles_per_mat * G.batch;
+      a.split.q[k] = tiles / 8;
+      a.split.r[k] = tiles % 8;
+      a.split.off[k] = left % 8;
+      left += tiles % 8;
+      total += tiles;
+    }
+    const bool multi = a.split.n > 1;
+    if (mode == GRAM && multi)
+      hipLaunchKernelGGL((ns_sym_bf16<GRAM, true>), dim3(total), dim3(256), 0, s, a);
+    else if (mode == GRAM)
+      hipLaunchKernelGGL((ns_sym_bf16<GRAM, false>), dim3(total), dim3(256), 0, s, a);
+    else if (multi)
+      hipLaunchKernelGGL((ns_sym_bf16<POLY, true>), dim3(total), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((ns_sym_bf16<POLY, false>), dim3(total), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
+
+// splits the groups of a call between the 256-tile kernel and this one
+hipError_t launch_sym(const NsGroup* groups, int n, int mode, float ca, float cb, float cc,
+                      hipStream_t s) {
   std::vector<NsGroup> big;
+  std::vector<const NsGroup*> small;
   for (int i = 0; i < n; ++i) {
     if (use_sym256(groups[i])) big.push_back(groups[i]);
-    else if (hipError_t e = launch_gram128(groups[i], s)) return e;
+    else small.push_back(groups + i);
   }
-  return big.empty() ? hipSuccess : launch_gram256_bf16(big.data(), (int)big.size(), s);
+  if (!small.empty())
+    if (hipError_t e = launch_sym128(small.data(), (int)small.size(), mode, ca, cb, cc, s))
+      return e;
+  if (big.empty()) return hipSuccess;
+  return mode == GRAM ? launch_gram256_bf16(big.data(), (int)big.size(), s)
+                      : launch_poly256_bf16(big.data(), (int)big.size(), ca, cb, cc, s);
+}
+
+}  // namespace
+
+hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s) {
+  return launch_sym(groups, n, GRAM, 0.f, 0.f, 0.f, s);
 }
 
 hipError_t launch_poly_bf16(const NsGroup* groups, int n, float ca, float cb, float cc,
                             hipStream_t s) {
-  std::vector<NsGroup> big;
-  for (int i = 0; i < n; ++i) {
-    if (use_sym256(groups[i])) big.push_back(groups[i]);
-    else if (hipError_t e = launch_poly128(groups[i], ca, cb, cc, s)) return e;
-  }
-  return big.empty() ? hipSuccess
-                     : launch_poly256_bf16(big.data(), (int)big.size(), ca, cb, cc, s);
+  return launch_sym(groups, n, POLY, ca, cb, cc, s);
 }
 
 }  // namespace muon

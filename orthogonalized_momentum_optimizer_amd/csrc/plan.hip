@@ -180,11 +180,27 @@ struct Launcher {
 
 // ---- the step ----------------------------------------------------------------------------
 
-// The step, group by group: momentum, norm, the Newton-Schulz rounds and the update of one
-// shape group before the next group starts. Consecutive launches of one group then find their
-// operands (X, A, B', at most ~60 MB for a group of GPT-2 matrices) still in the MI355X's
-// 256 MB Infinity Cache; running each phase over all groups before the next phase was
-// measured 3-6% slower per kernel.
+// Whether a step runs each phase over all shape groups together (one launch per product for
+// every group) instead of group by group. Group by group, consecutive launches of one group
+// find their operands (X, A, B', at most ~60 MB for a group of GPT-2 matrices) still in the
+// MI355X's 256 MB Infinity Cache, and running each phase over all groups was measured 3-6%
+// slower per kernel on the GPT-2-124M set (1296 apply tiles). A set too small to fill the
+// device group by group (one GPU's share of a data-parallel step: 6 x 768x768 + 3 x
+// 768x3072 leaves 54 and 108 apply tiles for 256 compute units) runs its groups side by side
+// instead: fewer than kMergeTilesPerCu apply tiles of 256x256 per compute unit in all.
+constexpr int kMergeTilesPerCu = 2;
+
+bool merge_groups(const muon_plan* p) {
+  if (p->prec == MUON_NS_F32_DEBUG || p->groups.size() < 2) return false;
+  long long tiles = 0;
+  for (const Group& G : p->groups)
+    tiles += (long long)((G.mp + 255) / 256) * ((G.np + 255) / 256) * G.count;
+  return tiles < (long long)kMergeTilesPerCu * device_cus();
+}
+
+// The step: momentum, norm, the Newton-Schulz rounds and the update of each shape group,
+// either one group after the other or, for small sets (merge_groups), phase by phase over all
+// groups.
 // grads: per matrix input (grad or NS input); moms: momentum (nullable array = no momentum
 // phase); params: W (nullable array = no update); outs: O destination (nullable entries);
 // out_param_dtype: O is written in the param dtype (else fp32).
@@ -196,15 +212,12 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
   const bool f32 = p->prec == MUON_NS_F32_DEBUG;
   const size_t esz = f32 ? 4 : 2;
   char* base = static_cast<char*>(ws);
+  auto xslot = [&](const Group& G) { return (size_t)G.mp * G.np * esz; };
+  auto scales_of = [&](const Group& G) { return reinterpret_cast<float*>(base + G.off_scales); };
 
-  for (size_t gi = 0; gi < p->groups.size(); ++gi) {
-    const Group& G = p->groups[gi];
-    char* x0 = base + G.off_x0;
+  // phase 1: momentum, norm partials, X0; then the norms
+  auto momentum_and_norm = [&](const Group& G) {
     float* part = reinterpret_cast<float*>(base + G.off_part);
-    float* scales = reinterpret_cast<float*>(base + G.off_scales);
-    const size_t xslot = (size_t)G.mp * G.np * esz;
-
-    // phase 1: momentum, norm partials, X0
     for (int si : G.sets) {
       const LaunchSet& S = p->sets[si];
       for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
@@ -222,7 +235,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
         E.np = G.np;
         E.vec = (S.cols % 4) == 0;
         const int slot = S.slot0 + (int)q0;
-        E.x = x0 + (size_t)slot * xslot;
+        E.x = base + G.off_x0 + (size_t)slot * xslot(G);
         E.partials = part + (size_t)slot * G.tiles64;
         E.beta = cfg->beta;
         E.nesterov = cfg->nesterov ? 1 : 0;
@@ -230,37 +243,54 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
               [&] { return launch_momentum(E, S.gdt == MUON_DT_F32, f32, stream); });
       }
     }
-    L.run(MUON_KERNEL_NORM, "norm",
-          [&] { return launch_norm(part, G.tiles64, scales, G.count, cfg->eps, stream); });
+    L.run(MUON_KERNEL_NORM, "norm", [&] {
+      return launch_norm(part, G.tiles64, scales_of(G), G.count, cfg->eps, stream);
+    });
+  };
 
-    // phase 2: Newton-Schulz rounds, ping-pong between x0 and x1
-    NsGroup N{};
-    N.x_in = x0;
-    N.x_out = base + G.off_x1;
-    N.a = base + G.off_a;
-    N.b = base + G.off_b;
-    N.scales = scales;
-    N.batch = G.count;
-    N.mp = G.mp;
-    N.np = G.np;
+  // phase 2: Newton-Schulz rounds over the listed groups, ping-pong between x0 and x1; the
+  // bf16 products take all of them in one launch each. Returns where each group's result is.
+  auto rounds = [&](const std::vector<int>& gis) {
+    std::vector<NsGroup> N(gis.size());
+    for (size_t k = 0; k < gis.size(); ++k) {
+      const Group& G = p->groups[gis[k]];
+      N[k] = NsGroup{};
+      N[k].x_in = base + G.off_x0;
+      N[k].x_out = base + G.off_x1;
+      N[k].a = base + G.off_a;
+      N[k].b = base + G.off_b;
+      N[k].scales = scales_of(G);
+      N[k].batch = G.count;
+      N[k].mp = G.mp;
+      N[k].np = G.np;
+    }
+    const int n = (int)N.size();
     for (int r = 0; r < cfg->ns_steps; ++r) {
-      N.first = r == 0;
+      for (NsGroup& g : N) g.first = r == 0;
       const float* abc = cfg->schedule ? cfg->schedule + 3 * r : &cfg->a;
       const float ca = abc[0], cb = abc[1], cc = abc[2];
-      L.run(MUON_KERNEL_GRAM, "gram",
-            [&] { return f32 ? launch_gram_f32(N, stream) : launch_gram_bf16(&N, 1, stream); });
-      L.run(MUON_KERNEL_POLY, "poly", [&] {
-        return f32 ? launch_poly_f32(N, cb, cc, stream)
-                   : launch_poly_bf16(&N, 1, ca, cb, cc, stream);
-      });
-      L.run(MUON_KERNEL_APPLY, "apply", [&] {
-        return f32 ? launch_apply_f32(N, ca, stream) : launch_apply_bf16(&N, 1, stream);
-      });
-      std::swap(N.x_in, N.x_out);
+      if (f32) {
+        for (NsGroup& g : N) {
+          L.run(MUON_KERNEL_GRAM, "gram", [&] { return launch_gram_f32(g, stream); });
+          L.run(MUON_KERNEL_POLY, "poly", [&] { return launch_poly_f32(g, cb, cc, stream); });
+          L.run(MUON_KERNEL_APPLY, "apply", [&] { return launch_apply_f32(g, ca, stream); });
+        }
+      } else {
+        L.run(MUON_KERNEL_GRAM, "gram", [&] { return launch_gram_bf16(N.data(), n, stream); });
+        L.run(MUON_KERNEL_POLY, "poly",
+              [&] { return launch_poly_bf16(N.data(), n, ca, cb, cc, stream); });
+        L.run(MUON_KERNEL_APPLY, "apply", [&] { return launch_apply_bf16(N.data(), n, stream); });
+      }
+      for (NsGroup& g : N) std::swap(g.x_in, g.x_out);
     }
+    std::vector<char*> res(gis.size());
+    for (size_t k = 0; k < gis.size(); ++k) res[k] = static_cast<char*>(N[k].x_in);
+    return res;
+  };
 
-    // phase 3: row equaliser (optional), parameter update (and O output)
-    char* xres = static_cast<char*>(N.x_in);
+  // phase 3: row equaliser (optional), parameter update (and O output) from X = xres
+  auto finish = [&](const Group& G, char* xres) {
+    float* scales = scales_of(G);
     float* rowsum = reinterpret_cast<float*>(base + G.off_rowsum);
     float* rowf = reinterpret_cast<float*>(base + G.off_rowf);
     if (row_vars) {
@@ -276,7 +306,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
           E.mp = G.mp;
           E.np = G.np;
           const int slot = S.slot0 + (int)q0;
-          E.x = xres + (size_t)slot * xslot;
+          E.x = xres + (size_t)slot * xslot(G);
           E.scales = scales + 4 * (size_t)slot;
           E.apply_scale = cfg->ns_steps == 0;
           E.rowsum = rowsum + (size_t)slot * kRowParts * G.np;
@@ -306,7 +336,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
         E.np = G.np;
         E.vec = (S.cols % 4) == 0;
         const int slot = S.slot0 + (int)q0;
-        E.x = xres + (size_t)slot * xslot;
+        E.x = xres + (size_t)slot * xslot(G);
         E.scales = scales + 4 * (size_t)slot;
         E.apply_scale = cfg->ns_steps == 0;
         E.lr = cfg->lr;
@@ -316,7 +346,22 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
               [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
       }
     }
-    if (L.status != MUON_OK) return L.status;
+  };
+
+  const int ng = (int)p->groups.size();
+  if (merge_groups(p)) {
+    std::vector<int> all(ng);
+    for (int gi = 0; gi < ng; ++gi) {
+      all[gi] = gi;
+      momentum_and_norm(p->groups[gi]);
+    }
+    const std::vector<char*> res = rounds(all);
+    for (int gi = 0; gi < ng; ++gi) finish(p->groups[gi], res[gi]);
+  } else {
+    for (int gi = 0; gi < ng && L.status == MUON_OK; ++gi) {
+      momentum_and_norm(p->groups[gi]);
+      finish(p->groups[gi], rounds({gi})[0]);
+    }
   }
   return L.status;
 }

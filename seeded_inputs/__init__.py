@@ -17,6 +17,9 @@ Workloads (the matrix shapes of GPT-2-style models; the pages train GPT-2 124M a
   gpt2_124m        12 layers x (Q, K, V, O 768x768; fc 3072x768; proj 768x3072) bf16
   tall_stress      48 x 3072x768 + 48 x 768x3072 bf16; heavy-tailed gradient rows
   gpt2_1p5b        48 layers x (4 x 1600x1600; fc 6400x1600; proj 1600x6400) bf16
+  gpt2_124m_shareN the matrices of gpt2_124m that rank 0 of N GPUs owns (N = 2, 4, 8) when
+                   whole matrices are dealt out round-robin within each size group (one GPU's
+                   share of a data-parallel step, at its real shapes); fresh draws
 
 W ~ N(0, 0.02) everywhere (0.02 is the standard deviation). The heavy-tailed rows of
 ``tall_stress`` are g_ij = 1e-3 * |t_i| * z_ij with t_i ~ Student-t(3) per row and
@@ -82,7 +85,25 @@ def _build() -> dict:
     s, lab = _gpt2_layer_shapes(1600)
     w["gpt2_1p5b"] = Workload("gpt2_1p5b", 4, tuple(s * 48), "bf16", 10, 1e-3,
                               labels=tuple(f"l{i}.{x}" for i in range(48) for x in lab))
+    full = w["gpt2_124m"]
+    for cid, world in ((5, 2), (6, 4), (7, 8)):
+        own = owned_indices(full.shapes, world, 0)
+        name = f"gpt2_124m_share{world}"
+        w[name] = Workload(name, cid, tuple(full.shapes[i] for i in own), "bf16", 20, 1e-3,
+                           labels=tuple(full.labels[i] for i in own))
     return w
+
+
+def owned_indices(shapes, world: int, rank: int) -> List[int]:
+    """The matrices ``rank`` of ``world`` GPUs owns when whole matrices are dealt out
+    round-robin within each size group (matrices of equal element count, in their original
+    order; groups in order of first appearance): positions p with p % world == rank."""
+    if not 0 <= rank < world:
+        raise ValueError("rank must be in [0, world)")
+    groups: dict = {}
+    for i, (r, c) in enumerate(shapes):
+        groups.setdefault(r * c, []).append(i)
+    return sorted(i for idx in groups.values() for p, i in enumerate(idx) if p % world == rank)
 
 
 WORKLOADS = _build()

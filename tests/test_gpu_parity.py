@@ -100,6 +100,31 @@ def test_gpt2_124m_full_size_f32_debug_sampled():
     compare(wl, gpu, 2, "f32")
 
 
+def test_gpt2_124m_share8_all_matrices():
+    """One GPU's share at 8 GPUs (6 x 768x768 + 3 x 3072x768): few tiles per launch, every
+    matrix compared over 3 steps."""
+    wl = si.WORKLOADS["gpt2_124m_share8"]
+    _announce("gpt2_124m_share8, all matrices")
+    gpu = run_gpu(wl, 3, "bf16")
+    compare(wl, gpu, 3, "bf16")
+
+
+def test_groups_side_by_side_equal_group_by_group_bitwise():
+    """A set too small to fill the device runs each phase over all shape groups at once; a
+    larger one runs group by group. The same 9 matrices (6 x 768x768, 3 x 3072x768; 162
+    apply tiles) alone and followed by 60 more 768x768 matrices (702 apply tiles) must give
+    bitwise the same W, M and O."""
+    _announce("side-by-side groups vs group by group")
+    small = [(768, 768)] * 6 + [(3072, 768)] * 3
+    a = run_gpu(si.custom(small, cfg_id=113, steps=2), 2, "bf16")
+    b = run_gpu(si.custom(small + [(768, 768)] * 60, cfg_id=113, steps=2), 2, "bf16",
+                watch=range(len(small)))
+    for i in range(len(small)):
+        for t in range(2):
+            for x, y in zip(a[i][t], b[i][t]):
+                assert np.array_equal(x, y), f"matrix {i} step {t}"
+
+
 def test_tall_stress_full_size_sampled():
     wl = si.WORKLOADS["tall_stress"]
     watch = si.sample_indices(wl)
