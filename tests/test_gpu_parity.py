@@ -125,6 +125,18 @@ def test_groups_side_by_side_equal_group_by_group_bitwise():
                 assert np.array_equal(x, y), f"matrix {i} step {t}"
 
 
+def test_more_groups_than_one_launch_holds():
+    """Ten small shape groups (padded mp 128-512), too few tiles to fill the device, so they
+    run side by side: the Gram and polynomial launches hold at most 8 groups (two launches
+    here), apply takes the groups of each mp together. Every element is compared."""
+    _announce("ten groups side by side")
+    shapes = [(128, 128), (128, 256), (128, 384), (256, 256), (256, 512), (384, 384),
+              (512, 128), (256, 384), (384, 512), (512, 512), (300, 40)]
+    wl = si.custom(shapes, cfg_id=114, steps=2)
+    gpu = run_gpu(wl, 2, "bf16")
+    compare(wl, gpu, 2, "bf16")
+
+
 def test_tall_stress_full_size_sampled():
     wl = si.WORKLOADS["tall_stress"]
     watch = si.sample_indices(wl)
