@@ -22,7 +22,10 @@
 //
 // With the MFMA operands passed as (right, left), accumulator block (i, j) holds the
 // transposed product: element r of lane l is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4],
-// so each register quad is 4 consecutive columns of one row: one 8-byte store.
+// so each register quad is 4 consecutive columns of one row. The epilogue pairs quads across
+// the two lane halves (v_permlane32_swap) so that every lane stores 16 bytes, 8 columns of
+// one row: with the tiled output layout that is a contiguous chunk, written straight from
+// registers with no LDS staging and no barrier.
 #include <algorithm>
 #include <vector>
 
@@ -81,14 +84,13 @@ __device__ __forceinline__ const T* kernel_args() {
   return (const T*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-// Output staging of the epilogue: 64 rows x 256 columns of bf16 (32 KB) beside the ring.
-constexpr int kUnitsOut = 64 * TN / 8;
 
 // The kernel body. kMulti: the launch holds several groups (tile -> group lookup); a single
-// group's tiles skip the lookup and the dependent argument load it needs.
-template <bool kMulti>
+// group's tiles skip the lookup and the dependent argument load it needs. kScaled: the first
+// round, whose output is scaled by s1 (every group of a launch has its scales, or none has).
+template <bool kMulti, bool kScaled>
 __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
-  __shared__ u32x4 smem[NSTAGE * kUnitsStage + kUnitsOut];  // 128 KB ring + 32 KB staging
+  __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB ring
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -266,10 +268,6 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     if constexpr (more) ready(f0, a0, b0);
   };
 
-  // Epilogue staging: chunk i holds tile rows 32i..32i+31 and 128+32i..128+32i+31 (the
-  // rows of every wave's accumulator block row i), 512-byte rows with 16-byte chunk q of row
-  // r at q ^ (r & 15).
-
   int L = lo + k0;
   const int hi = lo + nt;
   if (L < hi) {
@@ -296,7 +294,7 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     iteration(KT - 1, std::false_type{}, std::false_type{});
 
     // every wave is done with the ring: the next tile's first stages load while this tile's
-    // output drains through the staging area
+    // output is stored
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int row0 = cur.row0, col0 = cur.col0, np = cur.np;
@@ -310,69 +308,72 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
         for (int op = 0; op < 8; ++op) dma_op(cur, st, op);
     }
 
-    // the scale is 1 after the first round: skip its multiplies there. Every LDS access
-    // below is inline assembly and the scale a scalar load, so nothing here waits for the
-    // next tile's loads.
-    const float s = scale ? scalar_load_f32(scale) : 1.f;
-    const uint32_t stb = lds0 + 16u * (NSTAGE * kUnitsStage);  // staging base, bytes
-    auto stage_chunk = [&](int i, auto scaled_t) {
-      constexpr bool scaled = decltype(scaled_t)::value;
-      const int cr = wr * 32 + (lane & 31);
+    // Only the first round's kernels (kScaled) multiply by s1, read with a scalar load;
+    // nothing below waits for the next tile's loads (the stores read registers only).
+    const float s = kScaled ? scalar_load_f32(scale) : 1.f;
+    // The tile is stored straight from the accumulators. Register quad q of lane l holds
+    // columns 8q + 4(l/32) .. +3 of row l%32 of a block; converted to bf16, quads q and q + 1
+    // (q even) are exchanged between the lane halves (v_permlane32_swap: the upper half of
+    // the first operand trades places with the lower half of the second), after which lane l
+    // holds columns 8q + 8(l/32) .. +7 of that row: one 16-byte segment of the tiled layout.
+    // Addresses: in the tiled layout, with mp and np multiples of 128, lane l's segment of
+    // block (i, j), quad pair q sits 64 np i + 2048 j + 16 q bytes after its segment of block
+    // (0, 0); a wave's 128 rows and a tile's right 128 columns are each wholly inside the
+    // padded matrix or wholly outside.
+    const int half = lane >> 5;
+    const bool rows_in = row0 + wr * 128 < g.mp, right_in = col0 + 128 < np;
+    char* const seg0 = reinterpret_cast<char*>(
+        out + toff(min(row0 + wr * 128 + (lane & 31), g.mp - 1), col0 + 32 * wc + 8 * half, np));
+    {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = 64 * j + 32 * wc + 8 * q + 4 * (lane >> 5);
-          float v[4];
+        for (int j = 0; j < 4; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = scaled ? acc[i][j][4 * q + e] * s : acc[i][j][4 * q + e];
-          ds_write_b64_at(stb + 512u * cr + 16u * ((col >> 3) ^ (cr & 15)) + 8u * ((col >> 2) & 1),
-                          u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+          for (int q = 0; q < 4; q += 2) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = acc[i][j][4 * q + e];
+              v[e] = kScaled ? x * s : x;
+            }
+            uint32_t lo[2] = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+            uint32_t hi[2] = {pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+              lo[d] = r[0];
+              hi[d] = r[1];
+            }
+            if (rows_in && (j < 2 || right_in))
+              *reinterpret_cast<u32x4*>(seg0 + (size_t)64 * np * i + 2048 * j + 16 * q) =
+                  u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
         }
-    };
-    // Barrier for the staging area only: waits for this wave's LDS accesses, not for its
-    // outstanding loads of the next tile (__syncthreads would wait for those too).
-    auto lds_barrier = [] {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    const int ch = t & 31;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i > 0) lds_barrier();  // the previous chunk has been read out
-      if (scale) stage_chunk(i, std::true_type{});
-      else stage_chunk(i, std::false_type{});
-      lds_barrier();
-      u32x4 w[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int cr = (t >> 5) + 8 * k;
-        w[k] = ds_read_b128_at<0>(stb + 512u * cr + 16u * (ch ^ (cr & 15)));
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
-                     "+v"(w[6]), "+v"(w[7]));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int cr = (t >> 5) + 8 * k;
-        const int grow = row0 + 32 * i + (cr & 31) + 128 * (cr >> 5), gcol = col0 + 8 * ch;
-        if (grow < g.mp && gcol < np)
-          *reinterpret_cast<u32x4*>(out + toff(grow, gcol, np)) = w[k];
-      }
     }
   }
 }
 
-__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) { apply_tiles<false>(g); }
+__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) { apply_tiles<false, false>(g); }
 
-__global__ __launch_bounds__(256) void ns_apply_bf16_groups(ApplyArgs g) {
-  apply_tiles<true>(g);
+__global__ __launch_bounds__(256) void ns_apply_bf16_scaled(ApplyArgs g) {
+  apply_tiles<false, true>(g);
 }
 
-// launches the grid for a single group or for several
-void launch_apply_grid(const ApplyArgs& a, dim3 grid, hipStream_t s) {
-  if (a.n > 1) hipLaunchKernelGGL(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
+__global__ __launch_bounds__(256) void ns_apply_bf16_groups(ApplyArgs g) {
+  apply_tiles<true, false>(g);
+}
+
+__global__ __launch_bounds__(256) void ns_apply_bf16_groups_scaled(ApplyArgs g) {
+  apply_tiles<true, true>(g);
+}
+
+// launches the grid for a single group or for several, first round (scaled) or not
+void launch_apply_grid(const ApplyArgs& a, bool scaled, dim3 grid, hipStream_t s) {
+  if (a.n > 1 && scaled) hipLaunchKernelGGL(ns_apply_bf16_groups_scaled, grid, dim3(256), 0, s, a);
+  else if (a.n > 1) hipLaunchKernelGGL(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
+  else if (scaled) hipLaunchKernelGGL(ns_apply_bf16_scaled, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(ns_apply_bf16, grid, dim3(256), 0, s, a);
 }
 
@@ -415,7 +416,7 @@ hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
       q.first = a.total_tiles;
       a.total_tiles += q.per_mat * G.batch;
     }
-    launch_apply_grid(a, dim3(std::min(a.total_tiles, device_cus())), s);
+    launch_apply_grid(a, a.g[0].scales != nullptr, dim3(std::min(a.total_tiles, device_cus())), s);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;
