@@ -14,9 +14,10 @@
 // are bf16 in HBM; products accumulate in fp32; epilogues run in fp32 and round to nearest
 // even.
 //
-// Both outputs are symmetric: only the upper 128x128 tiles (I <= J) are computed; each is
-// stored with its mirror, and a diagonal tile takes its lower triangle from its upper one,
-// so A and B' are exactly symmetric.
+// Both outputs are symmetric: only the upper 128x128 tiles (I <= J) are computed. The
+// epilogue rounds the tile to bf16 once, stages it in LDS and writes it twice (rows of tile
+// (I, J), and its transpose as tile (J, I), read with transposing LDS loads); a diagonal
+// tile takes its lower triangle from its upper one, so A and B' are exactly symmetric.
 //
 // Tiling: 256 threads (4 waves as 2x2), a 128x128 output tile per block, each wave 64x64
 // (2x2 blocks of v_mfma_f32_32x32x16_bf16). K advances 32 at a time through a ring of 4 LDS
@@ -56,21 +57,11 @@ struct SymLaunch {      // the shape groups of one launch, longest tiles (larges
   float a, b, c;        // POLY coefficients
 };
 
-// fp32 staging tile of the epilogue: 128 rows of 32 chunks of 4 floats. Chunk q of row r is
-// stored at q ^ f(r) ^ (q >> 4) with f(r) = (r ^ (r >> 3)) & 15, so that 16 lanes writing one
-// chunk of 16 consecutive rows, reading the even (or odd) chunks of one row, or reading one
-// column of rows 8 apart each touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int stage_idx(int row, int col) {
-  const int q = col >> 2;
-  const int pq = q ^ ((row ^ (row >> 3)) & 15) ^ ((q >> 4) & 1);
-  return row * 128 + ((pq << 2) | (col & 3));
-}
-
-__device__ __forceinline__ u32x4 pack_bf16x8(const float v[8]) {
-  u32x4 o;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
-  return o;
+// Byte offset of element (row, col) in the epilogue's bf16 staging tile: 128 rows of 256
+// bytes, 16-byte chunk q of row r stored at q ^ (r & 15), so that 16 lanes reading the 16
+// chunks of one row, or one chunk of 16 consecutive rows, touch 16 distinct bank groups.
+__device__ __forceinline__ uint32_t stage_byte(int row, int col) {
+  return 256u * row + 16u * ((col >> 3) ^ (row & 15)) + 2u * (col & 7);
 }
 
 // kMulti: the launch holds several groups (block -> group lookup); a single group's blocks
@@ -103,13 +94,21 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
 
   const uint16_t* src = g.in + bidx * g.in_bs;
 
-  // POLY's b A term: A[I-tile rows][J-tile cols] passes through the left-operand stages
-  // 4J..4J+3 (A's I-tile rows at column block 4J + s); it is captured there in the
-  // epilogue's layout: thread t keeps 8-column chunk t%16 of rows t/16 + 16k, which arrives
-  // at stage 4J + (t%16)/4.
-  u32x4 epre[8];
+  // POLY's b A term: the elements of A[I-tile rows][J-tile cols] this lane's accumulators
+  // hold (4 consecutive columns of one row per register quad, 8 bytes of the tiled layout),
+  // loaded before the K loop's first loads so that they have long arrived by the epilogue.
+  u32x2 apre[2][2][4];
+  if constexpr (MODE == POLY) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) epre[k] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          apre[i][j][q] = *reinterpret_cast<const u32x2*>(
+              src + toff(I * BM + wr * 64 + 32 * i + (lane & 31),
+                         J * BN + wc * 64 + 32 * j + 8 * q + 4 * (lane >> 5), g.ld_in));
+  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -168,13 +167,6 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
 
       const u32x4* A = smem + (kt % STAGES) * kStage;
       const u32x4* B = kDiag ? A : A + 512;
-      if (MODE == POLY && (kt >> 2) == J && (kt & 3) == ((t & 15) >> 2)) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int row = (t >> 4) + 16 * k;
-          epre[k] = A[row * 4 + ((t & 3) ^ kswz(row))];
-        }
-      }
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int c = 2 * ks + (lane >> 5);
@@ -204,79 +196,109 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
   // all waves are done reading the operand stages before the epilogue reuses them
   __syncthreads();
 
-  // Epilogue, staged through LDS so that every global access is a 16-byte row segment. With
-  // the MFMA operands passed as (right, left), block (i, j) holds the transposed product:
-  // element r of lane l is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4], four consecutive
-  // columns per register quad, one 16-byte LDS write each.
-  float* st = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wr * 64 + i * 32 + (lane & 31);
-        const int col = wc * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                         acc[i][j][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(st + stage_idx(row, col)) = v;
-      }
-  __syncthreads();
-
-  const float s = (MODE == GRAM && g.scales) ? g.scales[4 * bidx + 1] : 1.f;
+  // Epilogue. With the MFMA operands passed as (right, left), element r of lane l of block
+  // (i, j) is C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4] of the wave's 64x64 quarter. The
+  // final values (Gram: s2 C; poly: b A + c C, plus a on the diagonal) are formed in fp32,
+  // rounded to bf16 once and staged; the tile is then written twice: rows of tile (I, J),
+  // and its transpose as tile (J, I), read with transposing LDS loads. A diagonal tile writes
+  // its upper triangle from its rows and its lower triangle from the transpose, so A and B'
+  // are exactly symmetric.
   uint16_t* out = g.out + bidx * (size_t)g.mp * g.mp;
-  const int ld = g.mp;
+  const int mp = g.mp, row0 = I * BM, col0 = J * BN;
   const bool diag = I == J;
-
-  // Row pass: output tile (I, J), chunk t%16 of rows t/16 + 16k. A diagonal tile takes its
-  // lower triangle from the upper triangle's accumulators (the b A term is symmetric too).
-  // Off-diagonal tiles write their final values back over their own staging slots for the
-  // mirror pass.
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MUON_LDS_PTR(smem)));
+  char* const stb = reinterpret_cast<char*>(smem);
+  {
+    const float s = (MODE == GRAM && g.scales) ? g.scales[4 * bidx + 1] : 1.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = (t >> 4) + 16 * k, ch = t & 15;
-    float a[8];
-    if (diag) {
+    for (int i = 0; i < 2; ++i) {
+      const int lr = wr * 64 + 32 * i + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = 8 * ch + e;
-        a[e] = col >= row ? st[stage_idx(row, col)] : st[stage_idx(col, row)];
-      }
-    } else {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(st + stage_idx(row, 8 * ch));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(st + stage_idx(row, 8 * ch + 4));
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
-    }
-    float v[8];
+        for (int q = 0; q < 4; ++q) {
+          const int lc = wc * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
+          float v[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (MODE == GRAM) {
-        v[e] = a[e] * s;
-      } else {
-        const uint32_t w = epre[k][e >> 1];
-        const float x = bf2f((e & 1) ? (w >> 16) : (w & 0xffffu));
-        v[e] = fmaf(S.b, x, S.c * a[e]);
-        if (diag && 8 * ch + e == row) v[e] += S.a;
-      }
-    }
-    *reinterpret_cast<u32x4*>(out + toff(I * BM + row, J * BN + 8 * ch, ld)) = pack_bf16x8(v);
-    if (!diag) {
-      *reinterpret_cast<f32x4*>(st + stage_idx(row, 8 * ch)) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(st + stage_idx(row, 8 * ch + 4)) = f32x4{v[4], v[5], v[6], v[7]};
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (MODE == GRAM) {
+              v[e] = acc[i][j][4 * q + e] * s;
+            } else {
+              const uint32_t w = apre[i][j][q][e >> 1] >> (16 * (e & 1));
+              v[e] = fmaf(S.b, bf2f(w & 0xffffu), S.c * acc[i][j][4 * q + e]);
+              if (diag && lr == lc + e) v[e] += S.a;
+            }
+          }
+          *reinterpret_cast<u32x2*>(stb + stage_byte(lr, lc)) =
+              u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
     }
   }
+  __syncthreads();
 
-  // Mirror pass: tile (J, I) is the transpose of the finished tile (I, J).
-  if (!diag) {
-    __syncthreads();
+  // Row pass: tile (I, J), 16-byte chunk t%16 of rows t/16 + 16k. A diagonal tile writes
+  // here only the chunks that start on or above the diagonal.
+  {
+    const int ch = t & 15;
+    u32x4 w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int col = (t >> 4) + 16 * k, ch = t & 15;  // output row = col, columns = rows
-      float v[8];
+      const int r = (t >> 4) + 16 * k;
+      w[k] = smem[r * 16 + (ch ^ (r & 15))];
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = st[stage_idx(8 * ch + e, col)];
-      *reinterpret_cast<u32x4*>(out + toff(J * BN + col, I * BM + 8 * ch, ld)) = pack_bf16x8(v);
+    for (int k = 0; k < 8; ++k) {
+      const int r = (t >> 4) + 16 * k;
+      if (!diag || 8 * ch >= r)
+        *reinterpret_cast<u32x4*>(out + toff(row0 + r, col0 + 8 * ch, mp)) = w[k];
+    }
+  }
+  // Transpose pass: tile (J, I) row R = staged column R, 8 columns = staged rows r0..r0+7.
+  // In each 16-lane group, lane 4e + q points at 4 staged columns c0 + 4q.. of row r0 + e
+  // (then r0 + 4 + e), and the transposing read gives lane i column c0 + i of those rows.
+  // One wave instruction pair covers 16 rows x 32 columns of the output; 4 in flight.
+  {
+    const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int ib = 0; ib < 8; ib += 4) {
+      s16x4 lo[4], hi[4];
+      u32x4 rowv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int combo = 8 * wave + ib + u;
+        const int c0 = 16 * (combo >> 2), r0 = 32 * (combo & 3) + 8 * grp;
+        const int ar = r0 + (li >> 2), acol = c0 + 4 * (li & 3);
+        lo[u] = ds_read_tr_at<0>(lds0 + stage_byte(ar, acol));
+        hi[u] = ds_read_tr_at<0>(lds0 + stage_byte(ar + 4, acol));
+        // row R's own values of the chunk (used where a diagonal tile's chunk crosses the
+        // diagonal); read unconditionally: a read issued on one path only would let the
+        // compiler copy its not-yet-arrived result at the join
+        rowv[u] = ds_read_b128_at<0>(lds0 + stage_byte(c0 + li, r0));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]), "+v"(hi[0]),
+                     "+v"(hi[1]), "+v"(hi[2]), "+v"(hi[3]), "+v"(rowv[0]), "+v"(rowv[1]),
+                     "+v"(rowv[2]), "+v"(rowv[3]));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int combo = 8 * wave + ib + u;
+        const int c0 = 16 * (combo >> 2), r0 = 32 * (combo & 3) + 8 * grp;
+        const int R = c0 + li;
+        if (diag && r0 >= R) continue;  // written by the row pass
+        const s16x8 tv = {lo[u][0], lo[u][1], lo[u][2], lo[u][3],
+                          hi[u][0], hi[u][1], hi[u][2], hi[u][3]};
+        u32x4 w = __builtin_bit_cast(u32x4, tv);
+        if (diag && R <= r0 + 7) {  // the diagonal crosses this chunk: upper part from row R
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t keep_lo = r0 + 2 * e < R ? 0x0000ffffu : 0u;
+            const uint32_t keep_hi = r0 + 2 * e + 1 < R ? 0xffff0000u : 0u;
+            const uint32_t keep = keep_lo | keep_hi;
+            w[e] = (w[e] & keep) | (rowv[u][e] & ~keep);
+          }
+        }
+        *reinterpret_cast<u32x4*>(out + toff(col0 + R, row0 + r0, mp)) = w;
+      }
     }
   }
 }
