@@ -95,20 +95,28 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
   const uint16_t* src = g.in + bidx * g.in_bs;
 
   // POLY's b A term: the elements of A[I-tile rows][J-tile cols] this lane's accumulators
-  // hold (4 consecutive columns of one row per register quad, 8 bytes of the tiled layout),
-  // loaded before the K loop's first loads so that they have long arrived by the epilogue.
+  // hold (4 consecutive columns of one row per register quad, 8 bytes of the tiled layout).
+  // They are loaded right after the last refill, so that they arrive while the last three
+  // stages compute and the first stages' loads do not queue behind them; the tail stages'
+  // waits leave these kPre loads pending (the memory clobbers keep the compiler from moving
+  // them, and tests/test_asm_lds_waits.py checks that they compile to exactly kPre loads).
   u32x2 apre[2][2][4];
-  if constexpr (MODE == POLY) {
+  constexpr int kPre = MODE == POLY ? 16 : 0;
+  auto load_apre = [&]() {
+    if constexpr (MODE == POLY) {
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          apre[i][j][q] = *reinterpret_cast<const u32x2*>(
-              src + toff(I * BM + wr * 64 + 32 * i + (lane & 31),
-                         J * BN + wc * 64 + 32 * j + 8 * q + 4 * (lane >> 5), g.ld_in));
-  }
+          for (int q = 0; q < 4; ++q)
+            apre[i][j][q] = *reinterpret_cast<const u32x2*>(
+                src + toff(I * BM + wr * 64 + 32 * i + (lane & 31),
+                           J * BN + wc * 64 + 32 * j + 8 * q + 4 * (lane >> 5), g.ld_in));
+      asm volatile("" ::: "memory");
+    }
+  };
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -155,11 +163,12 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
 
     // One stage of the main loop. LATER: this wave's loads issued after stage kt's (two
     // stages while refills run, then one, then none), so stage kt is in once at most LATER
-    // stages' loads are pending; REFILL: whether stage kt + 3 is loaded into the buffer that
-    // every wave finished with before this stage's barrier.
+    // stages' loads are pending (plus POLY's kPre loads once the refills are over); REFILL:
+    // whether stage kt + 3 is loaded into the buffer that every wave finished with before
+    // this stage's barrier.
     auto stage = [&](int kt, auto later_t, auto refill_t) {
       constexpr int later = decltype(later_t)::value;
-      vm_wait<later * kLoads>();
+      vm_wait<later * kLoads + (decltype(refill_t)::value ? 0 : kPre)>();
       // every wave's loads of stage kt are visible, and every wave is done with stage kt - 1
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");  // no LDS access moves across the barrier
@@ -186,7 +195,9 @@ __global__ __launch_bounds__(256) void ns_sym_bf16(SymLaunch S) {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     int kt = 0;
-    for (; kt < KT - (STAGES - 1); ++kt) stage(kt, I2{}, std::true_type{});
+    for (; kt < KT - STAGES; ++kt) stage(kt, I2{}, std::true_type{});
+    stage(kt++, I2{}, std::true_type{});
+    load_apre();
     stage(kt++, I2{}, std::false_type{});
     stage(kt++, I1{}, std::false_type{});
     stage(kt, I0{}, std::false_type{});

@@ -40,3 +40,56 @@ def test_checker_honours_partial_waits():
     ])
     v = asm_check.violations(text)
     assert len(v) == 1 and "v21" in v[0]
+
+
+def _vm_sequence(func_text):
+    """Vector-memory loads and vmcnt waits of one function, in program order: 'L' a
+    direct-to-LDS load, 'P' an 8-byte global load, ('W', n) a wait for vmcnt <= n."""
+    import re
+    seq = []
+    for ln in func_text.splitlines():
+        t = ln.strip()
+        if t.startswith("global_load_lds"):
+            seq.append("L")
+        elif t.startswith("global_load_dwordx2"):
+            seq.append("P")
+        elif t.startswith("s_waitcnt") and "vmcnt" in t:
+            seq.append(("W", int(re.search(r"vmcnt\((\d+)\)", t).group(1))))
+    return seq
+
+
+def test_poly_b_a_loads_match_the_tail_waits():
+    """The 128-tile polynomial kernel issues its 16 loads of the b A term right after the last
+    refill and its three tail stages wait with those 16 still pending: the compiled code must
+    hold exactly 16 such loads behind the refill's direct loads, followed by the waits
+    2k + 16, k + 16, 16 (k = direct loads per wave per stage: 4, or 2 on a diagonal tile)."""
+    import re
+    try:
+        path = build.device_asm("ns_gemm_bf16.hip")
+    except RuntimeError as e:
+        pytest.skip(str(e))
+    text = open(path).read()
+    funcs = re.split(r"\n(?=_Z\S+: ; @)", text)
+    poly = [f for f in funcs if f.startswith("_ZN4muon12_GLOBAL__N_111ns_sym_bf16ILi1")]
+    assert len(poly) == 2, [f.split(":")[0] for f in poly]   # single- and multi-group
+    for f in poly:
+        seq = _vm_sequence(f)
+        runs = [i for i in range(len(seq)) if seq[i] == "P" and (i == 0 or seq[i - 1] != "P")]
+        assert len(runs) == 2, "one run of b A loads per tile kind (diagonal, off-diagonal)"
+        ks = []
+        for i in runs:
+            n = 0
+            while seq[i + n] == "P":
+                n += 1
+            assert n == 16, n
+            k = 0
+            while seq[i - 1 - k] == "L":
+                k += 1
+            waits = [x[1] for x in seq[i + n:i + n + 3]]
+            assert all(isinstance(x, tuple) for x in seq[i + n:i + n + 3]), seq[i + n:i + n + 3]
+            assert waits == [2 * k + 16, k + 16, 16], (k, waits)
+            ks.append(k)
+        assert sorted(ks) == [2, 4], ks
+    # the Gram kernels load no b A term
+    gram = [f for f in funcs if f.startswith("_ZN4muon12_GLOBAL__N_111ns_sym_bf16ILi0")]
+    assert gram and all("P" not in _vm_sequence(f) for f in gram)
