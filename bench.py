@@ -18,6 +18,11 @@ two staged gradient batches used alternately). Prints one JSON line:
              one launch per step, HBM bytes of the algorithm over the launch time; and the
              same Muon step with the per-row energy equaliser switched on (its extra cost)
 
+  library_ceiling  what the vendor GEMM library (hipBLASLt, through torch.bmm / torch.matmul)
+             reaches on the same box in the same run: the apply products of the workload's
+             shape groups as plain batched GEMMs, and one large 8192^3 GEMM; a comparison
+             only, nothing of the step runs through it
+
     python bench.py --adam-only     times only the cautious-Adam step (for profiling it)
 """
 from __future__ import annotations
@@ -57,6 +62,59 @@ def kind_work(wl, ns_steps=5):
         w["momentum"] += r * c * (esz + 8.0)
         w["update"] += r * c * (2.0 * esz)
     return w
+
+
+def library_ceiling(wl, dev, apply_tflops, iters=20):
+    """hipBLASLt (torch.bmm / torch.matmul, bf16 in, fp32 accumulate, bf16 out) on the apply
+    products of the workload's shape groups, X' = B' X with B' (batch x m x m) and X
+    (batch x m x n), m <= n, both operands contiguous; and one 8192^3 GEMM, the large-GEMM
+    rate of the same box. Random operands; a measurement beside the step, not part of it."""
+    groups = {}
+    for r, c in wl.shapes:
+        m, n = min(r, c), max(r, c)
+        groups[(m, n)] = groups.get((m, n), 0) + 1
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    per, tot_ms, tot_fl = {}, 0.0, 0.0
+    for (m, n), b in sorted(groups.items()):
+        B = torch.randn((b, m, m), device=dev, generator=gen).bfloat16()
+        X = torch.randn((b, m, n), device=dev, generator=gen).bfloat16()
+        Y = torch.empty((b, m, n), device=dev, dtype=torch.bfloat16)
+        ms = timed(lambda: torch.bmm(B, X, out=Y))
+        fl = 2.0 * b * m * m * n
+        per[f"{b}x{m}x{m} @ {b}x{m}x{n}"] = {"us": 1e3 * ms, "tflops": fl / ms / 1e9}
+        tot_ms += ms
+        tot_fl += fl
+        del B, X, Y
+    big = 8192
+    P = torch.randn((big, big), device=dev, generator=gen).bfloat16()
+    Q = torch.randn((big, big), device=dev, generator=gen).bfloat16()
+    R = torch.empty((big, big), device=dev, dtype=torch.bfloat16)
+    ms_big = timed(lambda: torch.matmul(P, Q, out=R))
+    del P, Q, R
+    torch.cuda.empty_cache()
+    lib_apply = tot_fl / tot_ms / 1e9
+    big_tf = 2.0 * big ** 3 / ms_big / 1e9
+    return {"kind": "hipBLASLt via torch.bmm / torch.matmul, bf16, same box and run",
+            "apply_shapes": per, "apply_shapes_tflops": lib_apply,
+            "gemm_8192_tflops": big_tf, "gemm_8192_frac_of_peak": big_tf / PEAK_BF16_TFLOPS,
+            "apply_kernel_tflops": apply_tflops,
+            "apply_kernel_over_library_same_shapes": (apply_tflops / lib_apply
+                                                      if apply_tflops else None),
+            "apply_kernel_over_gemm_8192": apply_tflops / big_tf if apply_tflops else None}
 
 
 KERNEL_SOURCES = {   # kernel kind -> the source file that defines its bf16 kernel
@@ -223,6 +281,8 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the vendor-library GEMM comparison")
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
     ap.add_argument("--no-roweq", action="store_true", help="skip the row-equaliser leg")
     ap.add_argument("--adam-only", action="store_true",
@@ -349,6 +409,11 @@ def main():
         next_rows["cautious_adam"] = bench_adam(args.steps, args.warmup, dev)
     if next_rows:
         out["next_rows"] = next_rows
+    if not args.no_ceiling and args.precision == "bf16":
+        apply_tf = None
+        if "kernels" in out and out["kernels"]["apply"]["ms_per_step"] > 0:
+            apply_tf = work["apply"] / (out["kernels"]["apply"]["ms_per_step"] * 1e-3) / 1e12
+        out["library_ceiling"] = library_ceiling(wl, dev, apply_tf)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
