@@ -369,6 +369,182 @@ __global__ __launch_bounds__(256) void ns_apply_bf16_groups_scaled(ApplyArgs g) 
   apply_tiles<true, true>(g);
 }
 
+// ---- 128x128 tiles, for sets whose 256x256 tiles would leave most compute units idle ----
+// The same product on 128x128 output tiles, one tile per block (no persistent loop): 256
+// threads as 2x2 waves of 64 rows by two 32-column blocks at 64j + 32wc (2x2
+// v_mfma_f32_32x32x16_bf16 blocks, the 256-tile kernel's operand order and accumulator
+// layout), K in steps of 32 through a ring of 4 LDS stages of 16 KB (64 KB, two blocks per
+// CU). Per stage the left operand is 128 rows of B' x 32 K-values (K-contiguous, chunk
+// swizzle kswz) and the right operand 32 K-rows of X x 128 columns (N-contiguous, chunk
+// c of K-row k at c ^ 2(k & 3)), each filled by 2 direct-to-LDS loads per wave. Every output
+// element accumulates the same K slices in the same order with the same instruction as in
+// the 256-tile kernel, so the two kernels give bitwise the same X'.
+constexpr int SM = 128, SN = 128;
+constexpr int kSUnitsA = SM * TK / 8;                // 512 16-byte units
+constexpr int kSUnitsStage = kSUnitsA + TK * SN / 8;  // 1024 units, 16 KB
+constexpr int kSLoads = 4;                           // direct-to-LDS loads per wave per stage
+
+template <bool kScaled>
+__global__ __launch_bounds__(256) void ns_apply128_bf16(ApplyArgs g) {
+  __shared__ u32x4 smem[NSTAGE * kSUnitsStage];  // 64 KB ring
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+
+  // tile -> group (the last one whose first tile is at or below it), matrix and position
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxLaunchGroups; ++j)
+    if (j < g.n && L >= g.g[j].first) k = j;
+  const ApplyGroup& q = g.g[k];
+  const int l = L - q.first;
+  const int bidx = l / q.per_mat;
+  const int tt = l - bidx * q.per_mat;
+  const int I = tt / q.tiles_n, J = tt - (tt / q.tiles_n) * q.tiles_n;
+  const int mp = g.mp, np = q.np;
+  const size_t mn = (size_t)mp * np;
+  const char* lhs = reinterpret_cast<const char*>(q.b + bidx * (size_t)mp * mp);
+  const char* rhs = reinterpret_cast<const char*>(q.x + bidx * mn);
+  const size_t rhs_stage_bytes = (size_t)2 * TK * np;
+  const int row0 = I * SM, col0 = J * SN;
+  const int KT = mp / TK;  // >= 4: mp is a multiple of 128
+
+  // Loads 0-1 of a wave: 16 left-operand rows each (4 lanes x 16 bytes per row); loads 2-3:
+  // four right-operand K-rows each (16 lanes x 16 bytes per row). Lane l lands at 16 l of a
+  // 1 KB LDS block; the swizzle is applied by the global chunk a lane fetches.
+  uint32_t doff[4];
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const int row = 16 * (2 * wave + op) + (lane >> 2);
+    const int ch = (lane & 3) ^ kswz(row);
+    doff[op] = 2u * (uint32_t)toff(row0 + row, 8 * ch, mp);
+  }
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const int kk = 4 * (2 * wave + op) + (lane >> 4);
+    const int ch = (lane & 15) ^ (2 * (kk & 3));
+    doff[2 + op] = 2u * (uint32_t)toff(kk, col0 + 8 * ch, np);
+  }
+  auto issue = [&](int kt) {
+    u32x4* st = smem + (kt & (NSTAGE - 1)) * kSUnitsStage;
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+      __builtin_amdgcn_global_load_lds(lhs + (size_t)kt * kTileBytes + doff[op],
+                                       MUON_LDS_PTR(st + 64 * (2 * wave + op)), 16, 0, 0);
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+      __builtin_amdgcn_global_load_lds(rhs + (size_t)kt * rhs_stage_bytes + doff[2 + op],
+                                       MUON_LDS_PTR(st + kSUnitsA + 64 * (2 * wave + op)),
+                                       16, 0, 0);
+  };
+
+  // LDS read addresses (bytes from the stage origin). Left fragment i of slice ks: row
+  // wr*64 + 32i + l%32, chunk 2ks + l/32 (swizzled by bits 2-3 of the row, which 32i leaves
+  // alone): aoff + 2048 i + 32 ks bytes before the swizzle, so each ks has its own base.
+  // Right fragment j, half h of slice ks: columns 64j + 32wc + (16-column group), K-rows
+  // 16ks + 8(group/2) + 4h + 0..3: boff + 128 j + 1024 h + 4096 ks (j moves the chunk index
+  // by 8, above the bits the row swizzle changes; h and ks move whole groups of 4 rows).
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MUON_LDS_PTR(smem)));
+  const int arow = wr * 64 + (lane & 31);
+  const uint32_t aoff0 = 64 * arow + 16 * ((lane >> 5) ^ kswz(arow));
+  const uint32_t aoff1 = 64 * arow + 16 * ((2 + (lane >> 5)) ^ kswz(arow));
+  const int grp = lane >> 4, jj = lane & 15;
+  const int bn = 32 * wc + 16 * (grp & 1) + 4 * (jj & 3);
+  const int bk = 8 * (grp >> 1) + (jj >> 2);
+  const uint32_t boff =
+      16 * kSUnitsA + 2 * (bk * SN + 8 * ((bn >> 3) ^ (2 * (bk & 3))) + (bn & 7));
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // One K slice: 2 left and 4 transposing right reads, one wait that names them, 4 MFMAs.
+  auto slice = [&](uint32_t sb, auto ks_t) {
+    constexpr int ks = decltype(ks_t)::value;
+    const uint32_t va = sb + (ks ? aoff1 : aoff0), vb = sb + boff;
+    u32x4 av0 = ds_read_b128_at<0>(va);
+    u32x4 av1 = ds_read_b128_at<2048>(va);
+    s16x4 b00 = ds_read_tr_at<4096 * ks>(vb);
+    s16x4 b01 = ds_read_tr_at<1024 + 4096 * ks>(vb);
+    s16x4 b10 = ds_read_tr_at<128 + 4096 * ks>(vb);
+    s16x4 b11 = ds_read_tr_at<128 + 1024 + 4096 * ks>(vb);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(av0), "+v"(av1), "+v"(b00), "+v"(b01), "+v"(b10), "+v"(b11));
+    const bf16x8 af[2] = {__builtin_bit_cast(bf16x8, av0), __builtin_bit_cast(bf16x8, av1)};
+    const s16x8 v0 = {b00[0], b00[1], b00[2], b00[3], b01[0], b01[1], b01[2], b01[3]};
+    const s16x8 v1 = {b10[0], b10[1], b10[2], b10[3], b11[0], b11[1], b11[2], b11[3]};
+    const bf16x8 bf[2] = {__builtin_bit_cast(bf16x8, v0), __builtin_bit_cast(bf16x8, v1)};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  // One stage: LATER of this wave's loads issued after stage kt's (two while refills run,
+  // then one, then none) may still be pending; after the barrier every wave's loads of stage
+  // kt are visible and every wave has its reads of stage kt - 1 in registers, so that
+  // buffer takes stage kt + 3.
+  auto stage = [&](int kt, auto later_t, auto refill_t) {
+    constexpr int later = decltype(later_t)::value;
+    vm_wait<later * kSLoads>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+    if constexpr (decltype(refill_t)::value) issue(kt + NSTAGE - 1);
+    const uint32_t sb = lds0 + (uint32_t)((kt & (NSTAGE - 1)) * kSUnitsStage * 16);
+    slice(sb, std::integral_constant<int, 0>{});
+    slice(sb, std::integral_constant<int, 1>{});
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
+  int kt = 0;
+  for (; kt < KT - (NSTAGE - 1); ++kt) stage(kt, I2{}, std::true_type{});
+  stage(kt++, I2{}, std::false_type{});
+  stage(kt++, I1{}, std::false_type{});
+  stage(kt, I0{}, std::false_type{});
+
+  // Epilogue, straight from the accumulators as in the 256-tile kernel: quads q and q + 1
+  // (q even) are exchanged between the lane halves, after which lane l holds columns
+  // 8q + 8(l/32) .. +7 of row l%32 of block (i, j): 16 contiguous bytes of the tiled layout.
+  const float s = kScaled ? q.scales[4 * bidx] : 1.f;
+  uint16_t* const out = q.out + bidx * mn;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row0 + wr * 64 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int qq = 0; qq < 4; qq += 2) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = acc[i][j][4 * qq + e];
+          v[e] = kScaled ? x * s : x;
+        }
+        uint32_t lo[2] = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        uint32_t hi[2] = {pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto pr = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+          lo[d] = pr[0];
+          hi[d] = pr[1];
+        }
+        const int c = col0 + 64 * j + 32 * wc + 8 * qq + 8 * half;
+        *reinterpret_cast<u32x4*>(out + toff(r, c, np)) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+  }
+}
+
 // launches the grid for a single group or for several, first round (scaled) or not
 void launch_apply_grid(const ApplyArgs& a, bool scaled, dim3 grid, hipStream_t s) {
   if (a.n > 1 && scaled) hipLaunchKernelGGL(ns_apply_bf16_groups_scaled, grid, dim3(256), 0, s, a);
@@ -391,32 +567,49 @@ int device_cus() {
   return n;
 }
 
-// All groups of a call with the same mp in one persistent grid (their tiles all cost the
-// same: K = mp). A step calls with one group at a time unless its groups are too small to
-// fill the device on their own.
+// All groups of a call with the same mp in one grid (their tiles all cost the same:
+// K = mp): one persistent block per compute unit over 256x256 tiles, or, when those tiles
+// would leave at least half of the compute units idle, one block per 128x128 tile (four
+// times as many tiles, at most two blocks per compute unit). A step calls with one group at
+// a time unless its groups are too small to fill the device on their own.
 hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
+  const int cus = device_cus();
   std::vector<bool> done(n, false);
   for (int k0 = 0; k0 < n; ++k0) {
     if (done[k0]) continue;
-    ApplyArgs a{};
-    a.mp = groups[k0].mp;
-    a.tiles_m = (a.mp + TM - 1) / TM;
-    for (int k = k0; k < n && a.n < kMaxLaunchGroups; ++k) {
-      const NsGroup& G = groups[k];
-      if (done[k] || G.mp != a.mp) continue;
-      done[k] = true;
-      ApplyGroup& q = a.g[a.n++];
-      q.b = static_cast<const uint16_t*>(G.b);
-      q.x = static_cast<const uint16_t*>(G.x_in);
-      q.out = static_cast<uint16_t*>(G.x_out);
-      q.scales = G.first ? G.scales : nullptr;
-      q.np = G.np;
-      q.tiles_n = (G.np + TN - 1) / TN;
-      q.per_mat = a.tiles_m * q.tiles_n;
-      q.first = a.total_tiles;
-      a.total_tiles += q.per_mat * G.batch;
+    std::vector<const NsGroup*> set;
+    for (int k = k0; k < n && (int)set.size() < kMaxLaunchGroups; ++k)
+      if (!done[k] && groups[k].mp == groups[k0].mp) {
+        done[k] = true;
+        set.push_back(&groups[k]);
+      }
+    auto fill = [&](int tm, int tn) {
+      ApplyArgs a{};
+      a.mp = groups[k0].mp;
+      a.tiles_m = (a.mp + tm - 1) / tm;
+      for (const NsGroup* G : set) {
+        ApplyGroup& q = a.g[a.n++];
+        q.b = static_cast<const uint16_t*>(G->b);
+        q.x = static_cast<const uint16_t*>(G->x_in);
+        q.out = static_cast<uint16_t*>(G->x_out);
+        q.scales = G->first ? G->scales : nullptr;
+        q.np = G->np;
+        q.tiles_n = (G->np + tn - 1) / tn;
+        q.per_mat = a.tiles_m * q.tiles_n;
+        q.first = a.total_tiles;
+        a.total_tiles += q.per_mat * G->batch;
+      }
+      return a;
+    };
+    const ApplyArgs a = fill(TM, TN);
+    const bool scaled = a.g[0].scales != nullptr;
+    if (2 * a.total_tiles <= cus) {
+      const ApplyArgs h = fill(SM, SN);
+      if (scaled) hipLaunchKernelGGL(ns_apply128_bf16<true>, dim3(h.total_tiles), dim3(256), 0, s, h);
+      else hipLaunchKernelGGL(ns_apply128_bf16<false>, dim3(h.total_tiles), dim3(256), 0, s, h);
+    } else {
+      launch_apply_grid(a, scaled, dim3(std::min(a.total_tiles, cus)), s);
     }
-    launch_apply_grid(a, a.g[0].scales != nullptr, dim3(std::min(a.total_tiles, device_cus())), s);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

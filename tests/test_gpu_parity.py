@@ -167,6 +167,27 @@ def test_batch_equals_alone_bitwise():
                 assert np.array_equal(batch[i][t][k], alone[0][t][k]), (i, t, k)
 
 
+def test_apply_tile_sizes_agree_bitwise():
+    """A set whose 256x256 apply tiles would leave at least half of the compute units idle
+    runs 128x128 apply tiles instead. Both kernels add the same K slices in the same order,
+    so a matrix gives bitwise the same W, M and O alone (9 tiles of 256: the 128-tile
+    kernel) as inside a set of 20 (180 tiles of 256: the persistent 256-tile kernel); the
+    tall and wide 384x1536 pair checks a wide group and the transposed path the same way."""
+    _announce("apply 128 vs 256 tiles")
+    for shapes, watch in (([(768, 768)] * 20, (0, 13, 19)),
+                          ([(384, 1536), (1536, 384)] * 40, (0, 41, 79))):
+        wl = si.custom(shapes, dtype="bf16", steps=2, cfg_id=113)
+        batch = run_gpu(wl, 2, "bf16", watch=watch, gpu_fill_others=True)
+        for i in watch:
+            one = si.custom([shapes[i]], dtype="bf16", steps=2, cfg_id=113)
+            grads = [[si.grad(wl, i, t) for t in range(2)]]
+            alone = run_gpu(one, 2, "bf16", grads=grads, W0=[si.weight(wl, i)])
+            for t in range(2):
+                for k in range(3):
+                    assert np.array_equal(batch[i][t][k], alone[0][t][k]), (shapes[i], i, t, k)
+        compare(wl, {i: batch[i] for i in watch[:1]}, 2, "bf16")
+
+
 def test_deterministic_bitwise():
     _announce("determinism")
     wl = si.custom([(384, 640), (640, 384), (200, 200)], dtype="bf16", steps=2, cfg_id=104)
