@@ -46,6 +46,7 @@ class Workload:
     grad_std: float
     reuse_grad: bool = False                  # one gradient drawn once and reused every step
     heavy_tailed_rows: bool = False
+    iid_t3_entries: bool = False              # every entry grad_std * Student-t(3), independent
     labels: Tuple[str, ...] = field(default=())
 
     @property
@@ -135,7 +136,9 @@ def grad(wl: Workload, index: int, step: int):
     """Gradient of matrix ``index`` at step ``step`` (0-based) as a CPU torch tensor."""
     r, c = wl.shapes[index]
     g = rng(wl.cfg_id, KIND_GRAD, index, 0 if wl.reuse_grad else step)
-    if wl.heavy_tailed_rows:
+    if wl.iid_t3_entries:
+        x = wl.grad_std * g.standard_t(3, size=(r, c))
+    elif wl.heavy_tailed_rows:
         t = g.standard_t(3, size=(r, 1))
         z = g.standard_normal(size=(r, c))
         x = wl.grad_std * np.abs(t) * z
@@ -145,10 +148,12 @@ def grad(wl: Workload, index: int, step: int):
 
 
 def custom(shapes, dtype: str = "bf16", steps: int = 1, grad_std: float = 1e-3,
-           cfg_id: int = 100, heavy_tailed_rows: bool = False, reuse_grad: bool = False) -> Workload:
+           cfg_id: int = 100, heavy_tailed_rows: bool = False, reuse_grad: bool = False,
+           iid_t3_entries: bool = False) -> Workload:
     """An ad-hoc workload (ragged shapes, mixed sets) with the same seeding scheme."""
     return Workload(f"custom{cfg_id}", cfg_id, tuple(tuple(s) for s in shapes), dtype, steps,
-                    grad_std, reuse_grad=reuse_grad, heavy_tailed_rows=heavy_tailed_rows)
+                    grad_std, reuse_grad=reuse_grad, heavy_tailed_rows=heavy_tailed_rows,
+                    iid_t3_entries=iid_t3_entries)
 
 
 def sample_indices(wl: Workload) -> List[int]:

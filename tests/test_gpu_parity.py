@@ -82,6 +82,27 @@ def test_attn_768_workload(precision):
     compare(wl, gpu, steps, precision)
 
 
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_tiny_fp32_fresh_gradient_each_step(precision):
+    """The other reading of the 64x256 workload's text: a fresh N(0, 1) gradient every step
+    instead of one reused (the closed form above no longer applies; oracle parity does)."""
+    _announce(f"64x256 fp32, fresh gradient per step, {precision}")
+    wl = si.custom([(64, 256)], dtype="f32", steps=3, grad_std=1.0, cfg_id=114)
+    gpu = run_gpu(wl, 3, precision)
+    compare(wl, gpu, 3, precision)
+
+
+def test_iid_student_t_entries():
+    """The other reading of the tall-stress workload's "heavy-tailed rows": every gradient
+    entry i.i.d. 1e-3 * Student-t(3) (a few entries dominate the Frobenius norm), on two of
+    its matrices of each orientation, 3 steps, against the oracle."""
+    _announce("tall/wide 3072x768, i.i.d. Student-t(3) entries")
+    wl = si.custom([(3072, 768), (768, 3072)] * 2, dtype="bf16", steps=3, cfg_id=115,
+                   iid_t3_entries=True)
+    gpu = run_gpu(wl, 3, "bf16", watch=[0, 1])
+    compare(wl, gpu, 3, "bf16")
+
+
 def test_gpt2_124m_full_size_sampled():
     """All 72 matrices of the 124M set in one batched step; a sample of matrices of every
     shape is compared with the oracle (matrices are independent of each other)."""

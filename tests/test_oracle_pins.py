@@ -39,3 +39,14 @@ def test_heavy_tailed_rows():
     g = si.grad(wl, 0, 0).float().numpy()
     rms = np.sqrt((g ** 2).mean(axis=1))
     assert rms.max() / np.median(rms) > 5       # Student-t(3) row scales are heavy tailed
+
+
+def test_iid_student_t_entries():
+    wl = si.custom([(512, 64)], iid_t3_entries=True, cfg_id=4)
+    g = si.grad(wl, 0, 0).float().numpy()
+    a = np.abs(g).ravel()
+    # Student-t(3) entries: far heavier tails than a Gaussian of the same median size
+    assert a.max() / np.median(a) > 15
+    # but no row scaling: the row energies stay within a modest range of each other
+    rms = np.sqrt((g ** 2).mean(axis=1))
+    assert np.median(rms) > 0 and rms.min() / np.median(rms) > 0.3
