@@ -7,7 +7,8 @@ every matrix of the workload, on inputs already resident in HBM (weights, fp32 m
 two staged gradient batches used alternately). Prints one JSON line:
 
   value      Muon steps/s over K timed steps (HIP events on the library's stream,
-             bracketed by device synchronisation)
+             bracketed by device synchronisation); `repeats`: the median, min and max of
+             further timed passes of the same K steps (--repeats, default 5)
   roofline   the dominant kernel kind: algorithmic flops (or bytes) of its launches divided
              by their summed duration, measured with the library's per-launch HIP events in
              a second timed pass of the same K steps (its step time is reported as
@@ -151,29 +152,39 @@ def cpu_baseline(wl, budget_s=12.0):
     by nominal Newton-Schulz flops."""
     import numpy as np
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()
-                    if i.get("user_api") == "blas")
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(int(i.get("num_threads", 1)) for i in infos)
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in infos)
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     t0 = time.perf_counter()
     done_flops, used = 0.0, 0
     for i, (r, c) in enumerate(wl.shapes):
         W, G = si.weight(wl, i), si.grad(wl, i, 0)
-        t1 = time.perf_counter()
         oracle.muon_step(W, np.zeros((r, c)), G)
         m, n = min(r, c), max(r, c)
         done_flops += 5 * (4.0 * m * m * n + 2.0 * m ** 3)
         used = i + 1
         if time.perf_counter() - t0 > budget_s:
             break
-        del t1
     elapsed = time.perf_counter() - t0
     frac = done_flops / wl.ns_flops_per_step()
     sec_per_step = elapsed / frac
     return {"value": 1.0 / sec_per_step, "unit": "Muon steps/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas, "cpu_model": cpu_model,
+            "host_cpus": os.cpu_count(),
             "sample": f"float64 oracle, one step of matrices 0..{used - 1} of {wl.name} "
                       f"({used}/{wl.n} matrices, {frac * 100:.1f}% of the step's nominal flops,"
                       f" input generation included), scaled to the full step by flops; "
@@ -276,11 +287,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gpt2_124m", choices=sorted(si.WORKLOADS))
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="further timed passes of K steps after the reported one (median/min)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the vendor-library GEMM comparison")
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
@@ -345,6 +358,15 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
+    reps = []
+    for _ in range(args.repeats):
+        start.record(stream)
+        for t in range(args.steps):
+            plan.step(W, G[t % 2], M, cfg)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        reps.append(start.elapsed_time(stop) / args.steps)
+
     work = kind_work(wl)
     ns_flops = wl.ns_flops_per_step()
     out = {
@@ -359,6 +381,11 @@ def main():
                    "precision": args.precision},
         "ns_tflops_whole_step": ns_flops / (ms * 1e-3) / 1e12,
     }
+    if reps:
+        srt = sorted(reps)
+        out["repeats"] = {"n": len(reps), "steps_each": args.steps,
+                          "ms_per_step_median": srt[len(srt) // 2], "ms_per_step_min": srt[0],
+                          "ms_per_step_max": srt[-1]}
 
     if not args.no_profile:
         # a second timed pass of the same K steps with the library's per-launch HIP events

@@ -87,7 +87,7 @@ def test_tiny_fp32_fresh_gradient_each_step(precision):
     """The other reading of the 64x256 workload's text: a fresh N(0, 1) gradient every step
     instead of one reused (the closed form above no longer applies; oracle parity does)."""
     _announce(f"64x256 fp32, fresh gradient per step, {precision}")
-    wl = si.custom([(64, 256)], dtype="f32", steps=3, grad_std=1.0, cfg_id=114)
+    wl = si.custom([(64, 256)], dtype="f32", steps=3, grad_std=1.0, cfg_id=117)
     gpu = run_gpu(wl, 3, precision)
     compare(wl, gpu, 3, precision)
 
@@ -97,7 +97,7 @@ def test_iid_student_t_entries():
     entry i.i.d. 1e-3 * Student-t(3) (a few entries dominate the Frobenius norm), on two of
     its matrices of each orientation, 3 steps, against the oracle."""
     _announce("tall/wide 3072x768, i.i.d. Student-t(3) entries")
-    wl = si.custom([(3072, 768), (768, 3072)] * 2, dtype="bf16", steps=3, cfg_id=115,
+    wl = si.custom([(3072, 768), (768, 3072)] * 2, dtype="bf16", steps=3, cfg_id=118,
                    iid_t3_entries=True)
     gpu = run_gpu(wl, 3, "bf16", watch=[0, 1])
     compare(wl, gpu, 3, "bf16")
@@ -197,10 +197,10 @@ def test_apply_tile_sizes_agree_bitwise():
     _announce("apply 128 vs 256 tiles")
     for shapes, watch in (([(768, 768)] * 20, (0, 13, 19)),
                           ([(384, 1536), (1536, 384)] * 40, (0, 41, 79))):
-        wl = si.custom(shapes, dtype="bf16", steps=2, cfg_id=113)
+        wl = si.custom(shapes, dtype="bf16", steps=2, cfg_id=116)
         batch = run_gpu(wl, 2, "bf16", watch=watch, gpu_fill_others=True)
         for i in watch:
-            one = si.custom([shapes[i]], dtype="bf16", steps=2, cfg_id=113)
+            one = si.custom([shapes[i]], dtype="bf16", steps=2, cfg_id=116)
             grads = [[si.grad(wl, i, t) for t in range(2)]]
             alone = run_gpu(one, 2, "bf16", grads=grads, W0=[si.weight(wl, i)])
             for t in range(2):
