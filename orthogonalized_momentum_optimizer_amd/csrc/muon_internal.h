@@ -97,7 +97,8 @@ struct NsGroup {
 // too small to fill the device one by one). Gram and poly: groups with use_sym256
 // (mp >= 1024) share 256x256-tile launches (ns_sym256_bf16.hip), smaller groups 128x128-tile
 // launches (ns_gemm_bf16.hip); up to 8 groups per launch, tiles ordered longest first on
-// every XCD. Apply: 256x256 tiles, groups of equal mp in one persistent launch
+// every XCD. Apply: 256x256 tiles, groups of equal mp in one persistent launch, or 128x128
+// tiles (one block each) when the 256x256 tiles number at most half the compute units
 // (ns_apply_bf16.hip).
 bool use_sym256(const NsGroup& g);
 hipError_t launch_gram_bf16(const NsGroup* groups, int n, hipStream_t s);   // A = s2 X X^T

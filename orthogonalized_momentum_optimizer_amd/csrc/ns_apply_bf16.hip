@@ -26,6 +26,10 @@
 // the two lane halves (v_permlane32_swap) so that every lane stores 16 bytes, 8 columns of
 // one row: with the tiled output layout that is a contiguous chunk, written straight from
 // registers with no LDS staging and no barrier.
+//
+// Sets too small for 256x256 tiles to occupy half of the compute units (a single 768x768
+// matrix has 9) run a 128x128-tile version of the same product instead (ns_apply128_bf16,
+// below), bitwise equal to this one.
 #include <algorithm>
 #include <vector>
 
