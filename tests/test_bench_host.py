@@ -28,7 +28,7 @@ def test_kind_work_matches_the_nominal_count():
 
 def test_adam_bytes_per_element():
     assert bench.adam_bytes_per_element("bf16", "bf16") == 22   # 2+2+4+4 read, 2+4+4 written
-    assert bench.adam_bytes_per_element("f32", "f32") == 30
+    assert bench.adam_bytes_per_element("f32", "f32") == 28   # 4+4+4+4 read, 4+4+4 written
     assert bench.adam_bytes_per_element("f32", "bf16") == 26   # 4+2+4+4 read, 4+4+4 written
 
 
