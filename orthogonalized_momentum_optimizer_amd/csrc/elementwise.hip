@@ -8,9 +8,10 @@
 //
 // Layout: every kernel works on 64x64 tiles, 256 threads, each thread owning four
 // consecutive columns of four rows (rows t/16 + 16k, columns 4*(t%16)..+3), so a wavefront
-// reads 256 contiguous bytes of fp32 per row segment. Tall matrices are transposed through
-// an LDS tile so that both the original-orientation side and the wide-form side of the
-// copy stay coalesced.
+// reads 256 contiguous bytes of fp32 per row segment; the update of matrices whose column
+// count is a multiple of 8 uses eight columns of two rows per thread instead (16-byte bf16
+// accesses, measured 10% faster). Tall matrices are transposed through an LDS tile so that
+// both the original-orientation side and the wide-form side of the copy stay coalesced.
 #include "muon_internal.h"
 
 namespace muon {
@@ -355,6 +356,98 @@ __global__ __launch_bounds__(256) void update_kernel(ElemLaunch L) {
   }
 }
 
+// Eight consecutive elements (16 bytes of bf16, 32 of fp32) from an index that is a
+// multiple of 8.
+template <int DT>
+__device__ __forceinline__ void load8(const void* p, size_t i, float v[8]) {
+  if (DT == 0) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_bits_to_f32(u[k] & 0xffffu);
+      v[2 * k + 1] = bf16_bits_to_f32(u[k] >> 16);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* p, size_t i, const float v[8]) {
+  if (DT == 0) {
+    uint4 w;
+    w.x = pack_bf16(v[0], v[1]);
+    w.y = pack_bf16(v[2], v[3]);
+    w.z = pack_bf16(v[4], v[5]);
+    w.w = pack_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = w;
+  } else {
+    float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
+    q[0] = make_float4(v[0], v[1], v[2], v[3]);
+    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// The update for matrices whose cols is a multiple of 8: each thread owns eight consecutive
+// columns of two rows (rows t/8 + 32k, columns 8*(t%8)..+7), 16-byte bf16 accesses.
+template <int PDT, int ODT, int XDT>
+__global__ __launch_bounds__(256) void update_kernel8(ElemLaunch L) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int q = blockIdx.y;
+  const int t = threadIdx.x;
+  const int tiles_c = (L.cols + kTile - 1) / kTile;
+  const int r0 = (blockIdx.x / tiles_c) * kTile, c0 = (blockIdx.x % tiles_c) * kTile;
+  const void* x = static_cast<const char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
+  void* w = L.param[q];
+  void* o = L.out[q];
+  const float s = L.apply_scale ? L.scales[4 * q] : 1.f;
+  const float lr = L.lr;
+  const float* rowf = L.rowf ? L.rowf + (size_t)q * L.np : nullptr;
+
+  if (L.tall) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int a = (t >> 4) + 16 * k, b = 4 * (t & 15);
+      float v[4];
+      load4<XDT>(x, xidx<XDT>(c0 + a, r0 + b, L.np), v);  // within the padded buffer
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[a][b + e] = v[e];
+    }
+    __syncthreads();
+  }
+
+  const int lc = 8 * (t & 7);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int lr_ = (t >> 3) + 32 * k;
+    const int r = r0 + lr_, c = c0 + lc;
+    if (r >= L.rows || c >= L.cols) continue;  // cols % 8 == 0: the whole vector is inside
+    float ov[8];
+    if (L.tall) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] = tile[lc + e][lr_];
+    } else {
+      load8<XDT>(x, xidx<XDT>(r, c, L.np), ov);
+    }
+    const float sr = rowf ? s * rowf[r] : s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] *= sr;
+    const size_t base = (size_t)r * L.cols + c;
+    if (w) {
+      float wv[8];
+      load8<PDT>(w, base, wv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = fmaf(-lr, ov[e], wv[e]);
+      store8<PDT>(w, base, wv);
+    }
+    if (o) store8<ODT>(o, base, ov);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStream_t s) {
@@ -390,6 +483,19 @@ hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_dt, int x_f3
   const int tiles = ((L.rows + kTile - 1) / kTile) * ((L.cols + kTile - 1) / kTile);
   const dim3 grid(tiles, L.count), block(256);
   const int code = param_dt * 4 + out_dt * 2 + x_f32;
+  if (L.vec && (L.cols & 7) == 0) {
+    switch (code) {
+      case 0: hipLaunchKernelGGL((update_kernel8<0, 0, 0>), grid, block, 0, s, L); break;
+      case 1: hipLaunchKernelGGL((update_kernel8<0, 0, 1>), grid, block, 0, s, L); break;
+      case 2: hipLaunchKernelGGL((update_kernel8<0, 1, 0>), grid, block, 0, s, L); break;
+      case 3: hipLaunchKernelGGL((update_kernel8<0, 1, 1>), grid, block, 0, s, L); break;
+      case 4: hipLaunchKernelGGL((update_kernel8<1, 0, 0>), grid, block, 0, s, L); break;
+      case 5: hipLaunchKernelGGL((update_kernel8<1, 0, 1>), grid, block, 0, s, L); break;
+      case 6: hipLaunchKernelGGL((update_kernel8<1, 1, 0>), grid, block, 0, s, L); break;
+      default: hipLaunchKernelGGL((update_kernel8<1, 1, 1>), grid, block, 0, s, L); break;
+    }
+    return hipGetLastError();
+  }
   switch (code) {
     case 0: hipLaunchKernelGGL((update_kernel<0, 0, 0>), grid, block, 0, s, L); break;
     case 1: hipLaunchKernelGGL((update_kernel<0, 0, 1>), grid, block, 0, s, L); break;
