@@ -452,29 +452,29 @@ __global__ __launch_bounds__(256) void update_kernel8(ElemLaunch L) {
 
 hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStream_t s) {
   const dim3 grid((L.mp / kTile) * (L.np / kTile), L.count), block(256);
-  if (grad_dt == 0 && !x_f32) hipLaunchKernelGGL((momentum_kernel<0, 0>), grid, block, 0, s, L);
-  else if (grad_dt == 0) hipLaunchKernelGGL((momentum_kernel<0, 1>), grid, block, 0, s, L);
-  else if (!x_f32) hipLaunchKernelGGL((momentum_kernel<1, 0>), grid, block, 0, s, L);
-  else hipLaunchKernelGGL((momentum_kernel<1, 1>), grid, block, 0, s, L);
+  if (grad_dt == 0 && !x_f32) launch_k((momentum_kernel<0, 0>), grid, block, 0, s, L);
+  else if (grad_dt == 0) launch_k((momentum_kernel<0, 1>), grid, block, 0, s, L);
+  else if (!x_f32) launch_k((momentum_kernel<1, 0>), grid, block, 0, s, L);
+  else launch_k((momentum_kernel<1, 1>), grid, block, 0, s, L);
   return hipGetLastError();
 }
 
 hipError_t launch_norm(const float* partials, int tiles, float* scales, int count, float eps,
                        hipStream_t s) {
-  hipLaunchKernelGGL(norm_kernel, dim3(count), dim3(256), 0, s, partials, tiles, scales, eps);
+  launch_k(norm_kernel, dim3(count), dim3(256), 0, s, partials, tiles, scales, eps);
   return hipGetLastError();
 }
 
 hipError_t launch_rowstat(const ElemLaunch& L, int x_f32, hipStream_t s) {
   const int bx = L.tall ? (L.rows + 255) / 256 : (L.rows + 3) / 4;
   const dim3 grid(bx, L.count, L.tall ? kRowParts : 1), block(256);
-  if (x_f32) hipLaunchKernelGGL(rowstat_kernel<1>, grid, block, 0, s, L);
-  else hipLaunchKernelGGL(rowstat_kernel<0>, grid, block, 0, s, L);
+  if (x_f32) launch_k(rowstat_kernel<1>, grid, block, 0, s, L);
+  else launch_k(rowstat_kernel<0>, grid, block, 0, s, L);
   return hipGetLastError();
 }
 
 hipError_t launch_roweq_finish(const ElemLaunch& L, hipStream_t s) {
-  hipLaunchKernelGGL(roweq_finish_kernel, dim3(L.count), dim3(1024), 0, s, L);
+  launch_k(roweq_finish_kernel, dim3(L.count), dim3(1024), 0, s, L);
   return hipGetLastError();
 }
 
@@ -485,26 +485,26 @@ hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_dt, int x_f3
   const int code = param_dt * 4 + out_dt * 2 + x_f32;
   if (L.vec && (L.cols & 7) == 0) {
     switch (code) {
-      case 0: hipLaunchKernelGGL((update_kernel8<0, 0, 0>), grid, block, 0, s, L); break;
-      case 1: hipLaunchKernelGGL((update_kernel8<0, 0, 1>), grid, block, 0, s, L); break;
-      case 2: hipLaunchKernelGGL((update_kernel8<0, 1, 0>), grid, block, 0, s, L); break;
-      case 3: hipLaunchKernelGGL((update_kernel8<0, 1, 1>), grid, block, 0, s, L); break;
-      case 4: hipLaunchKernelGGL((update_kernel8<1, 0, 0>), grid, block, 0, s, L); break;
-      case 5: hipLaunchKernelGGL((update_kernel8<1, 0, 1>), grid, block, 0, s, L); break;
-      case 6: hipLaunchKernelGGL((update_kernel8<1, 1, 0>), grid, block, 0, s, L); break;
-      default: hipLaunchKernelGGL((update_kernel8<1, 1, 1>), grid, block, 0, s, L); break;
+      case 0: launch_k((update_kernel8<0, 0, 0>), grid, block, 0, s, L); break;
+      case 1: launch_k((update_kernel8<0, 0, 1>), grid, block, 0, s, L); break;
+      case 2: launch_k((update_kernel8<0, 1, 0>), grid, block, 0, s, L); break;
+      case 3: launch_k((update_kernel8<0, 1, 1>), grid, block, 0, s, L); break;
+      case 4: launch_k((update_kernel8<1, 0, 0>), grid, block, 0, s, L); break;
+      case 5: launch_k((update_kernel8<1, 0, 1>), grid, block, 0, s, L); break;
+      case 6: launch_k((update_kernel8<1, 1, 0>), grid, block, 0, s, L); break;
+      default: launch_k((update_kernel8<1, 1, 1>), grid, block, 0, s, L); break;
     }
     return hipGetLastError();
   }
   switch (code) {
-    case 0: hipLaunchKernelGGL((update_kernel<0, 0, 0>), grid, block, 0, s, L); break;
-    case 1: hipLaunchKernelGGL((update_kernel<0, 0, 1>), grid, block, 0, s, L); break;
-    case 2: hipLaunchKernelGGL((update_kernel<0, 1, 0>), grid, block, 0, s, L); break;
-    case 3: hipLaunchKernelGGL((update_kernel<0, 1, 1>), grid, block, 0, s, L); break;
-    case 4: hipLaunchKernelGGL((update_kernel<1, 0, 0>), grid, block, 0, s, L); break;
-    case 5: hipLaunchKernelGGL((update_kernel<1, 0, 1>), grid, block, 0, s, L); break;
-    case 6: hipLaunchKernelGGL((update_kernel<1, 1, 0>), grid, block, 0, s, L); break;
-    default: hipLaunchKernelGGL((update_kernel<1, 1, 1>), grid, block, 0, s, L); break;
+    case 0: launch_k((update_kernel<0, 0, 0>), grid, block, 0, s, L); break;
+    case 1: launch_k((update_kernel<0, 0, 1>), grid, block, 0, s, L); break;
+    case 2: launch_k((update_kernel<0, 1, 0>), grid, block, 0, s, L); break;
+    case 3: launch_k((update_kernel<0, 1, 1>), grid, block, 0, s, L); break;
+    case 4: launch_k((update_kernel<1, 0, 0>), grid, block, 0, s, L); break;
+    case 5: launch_k((update_kernel<1, 0, 1>), grid, block, 0, s, L); break;
+    case 6: launch_k((update_kernel<1, 1, 0>), grid, block, 0, s, L); break;
+    default: launch_k((update_kernel<1, 1, 1>), grid, block, 0, s, L); break;
   }
   return hipGetLastError();
 }

@@ -6,6 +6,7 @@
 // host has validated shapes, pointers and the workspace layout.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -114,5 +115,28 @@ hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, f
 hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);
 hipError_t launch_poly_f32(const NsGroup& g, float b, float c, hipStream_t s);
 hipError_t launch_apply_f32(const NsGroup& g, float a, hipStream_t s);
+
+// The library's per-launch timing (muon_plan_set_profiling). While one launcher call of a
+// step is timed, its first kernel launch records `start` when that kernel starts and every
+// launch records `stop` when it ends, taken from the kernel dispatches themselves (no marker
+// packets between the kernels, which would add their own latency to what is measured).
+// Both are null when nothing is timed; then, and under stream capture, launches are plain.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming g_launch_timing;
+
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                     hipStream_t s, Args... args) {
+  if (g_launch_timing.stop) {
+    hipEvent_t start = g_launch_timing.start;
+    g_launch_timing.start = nullptr;  // later launches of the same call extend `stop` only
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, start, g_launch_timing.stop, 0u,
+                          args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 }  // namespace muon

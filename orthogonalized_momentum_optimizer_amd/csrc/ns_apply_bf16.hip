@@ -551,10 +551,10 @@ __global__ __launch_bounds__(256) void ns_apply128_bf16(ApplyArgs g) {
 
 // launches the grid for a single group or for several, first round (scaled) or not
 void launch_apply_grid(const ApplyArgs& a, bool scaled, dim3 grid, hipStream_t s) {
-  if (a.n > 1 && scaled) hipLaunchKernelGGL(ns_apply_bf16_groups_scaled, grid, dim3(256), 0, s, a);
-  else if (a.n > 1) hipLaunchKernelGGL(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
-  else if (scaled) hipLaunchKernelGGL(ns_apply_bf16_scaled, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(ns_apply_bf16, grid, dim3(256), 0, s, a);
+  if (a.n > 1 && scaled) launch_k(ns_apply_bf16_groups_scaled, grid, dim3(256), 0, s, a);
+  else if (a.n > 1) launch_k(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
+  else if (scaled) launch_k(ns_apply_bf16_scaled, grid, dim3(256), 0, s, a);
+  else launch_k(ns_apply_bf16, grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -609,8 +609,8 @@ hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
     const bool scaled = a.g[0].scales != nullptr;
     if (2 * a.total_tiles <= cus) {
       const ApplyArgs h = fill(SM, SN);
-      if (scaled) hipLaunchKernelGGL(ns_apply128_bf16<true>, dim3(h.total_tiles), dim3(256), 0, s, h);
-      else hipLaunchKernelGGL(ns_apply128_bf16<false>, dim3(h.total_tiles), dim3(256), 0, s, h);
+      if (scaled) launch_k(ns_apply128_bf16<true>, dim3(h.total_tiles), dim3(256), 0, s, h);
+      else launch_k(ns_apply128_bf16<false>, dim3(h.total_tiles), dim3(256), 0, s, h);
     } else {
       launch_apply_grid(a, scaled, dim3(std::min(a.total_tiles, cus)), s);
     }

@@ -356,13 +356,13 @@ hipError_t launch_sym128(const NsGroup* const* groups, int n, int mode, float ca
     }
     const bool multi = a.split.n > 1;
     if (mode == GRAM && multi)
-      hipLaunchKernelGGL((ns_sym_bf16<GRAM, true>), dim3(total), dim3(256), 0, s, a);
+      launch_k((ns_sym_bf16<GRAM, true>), dim3(total), dim3(256), 0, s, a);
     else if (mode == GRAM)
-      hipLaunchKernelGGL((ns_sym_bf16<GRAM, false>), dim3(total), dim3(256), 0, s, a);
+      launch_k((ns_sym_bf16<GRAM, false>), dim3(total), dim3(256), 0, s, a);
     else if (multi)
-      hipLaunchKernelGGL((ns_sym_bf16<POLY, true>), dim3(total), dim3(256), 0, s, a);
+      launch_k((ns_sym_bf16<POLY, true>), dim3(total), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((ns_sym_bf16<POLY, false>), dim3(total), dim3(256), 0, s, a);
+      launch_k((ns_sym_bf16<POLY, false>), dim3(total), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

@@ -106,7 +106,7 @@ hipError_t launch_gram_f32(const NsGroup& G, hipStream_t s) {
   a.tiles_n = G.mp / TM;
   a.scales = G.first ? G.scales : nullptr;
   a.scale_idx = 1;
-  hipLaunchKernelGGL(ns_gemm_f32<GRAM>, dim3((G.mp / TM) * (G.mp / TM), G.batch), dim3(256), 0,
+  launch_k(ns_gemm_f32<GRAM>, dim3((G.mp / TM) * (G.mp / TM), G.batch), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -121,7 +121,7 @@ hipError_t launch_poly_f32(const NsGroup& G, float b, float c, hipStream_t s) {
   a.tiles_n = G.mp / TM;
   a.alpha = b;
   a.beta = c;
-  hipLaunchKernelGGL(ns_gemm_f32<POLY>, dim3((G.mp / TM) * (G.mp / TM), G.batch), dim3(256), 0,
+  launch_k(ns_gemm_f32<POLY>, dim3((G.mp / TM) * (G.mp / TM), G.batch), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -140,7 +140,7 @@ hipError_t launch_apply_f32(const NsGroup& G, float alpha, hipStream_t s) {
   a.scales = G.first ? G.scales : nullptr;
   a.scale_idx = 0;
   a.alpha = alpha;
-  hipLaunchKernelGGL(ns_gemm_f32<APPLY>, dim3((G.mp / TM) * (G.np / TM), G.batch), dim3(256), 0,
+  launch_k(ns_gemm_f32<APPLY>, dim3((G.mp / TM) * (G.np / TM), G.batch), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

@@ -420,9 +420,9 @@ hipError_t launch_sym256(const NsGroup* groups, int n, int mode, float ca, float
       total += tiles;
     }
     if (mode == GRAM)
-      hipLaunchKernelGGL(ns_sym256_bf16<GRAM>, dim3(total), dim3(256), 0, s, a);
+      launch_k(ns_sym256_bf16<GRAM>, dim3(total), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(ns_sym256_bf16<POLY>, dim3(total), dim3(256), 0, s, a);
+      launch_k(ns_sym256_bf16<POLY>, dim3(total), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

@@ -27,6 +27,8 @@ thread_local std::string g_last_error;
 
 namespace muon {
 
+thread_local LaunchTiming g_launch_timing;
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -164,14 +166,14 @@ struct Launcher {
   void run(int kind, const char* what, F&& f) {
     if (status != MUON_OK) return;
     const bool timed = p->prof && p->ev_used < (int)p->ev.size() / 2;
-    if (timed) (void)hipEventRecord(p->ev[2 * p->ev_used], s);
+    if (timed) g_launch_timing = {p->ev[2 * p->ev_used], p->ev[2 * p->ev_used + 1]};
     const hipError_t e = f();
+    g_launch_timing = {};
     if (e != hipSuccess) {
       status = fail(MUON_ERR_HIP, "launch of %s failed: %s", what, hipGetErrorString(e));
       return;
     }
     if (timed) {
-      (void)hipEventRecord(p->ev[2 * p->ev_used + 1], s);
       p->ev_kind[p->ev_used] = kind;
       ++p->ev_used;
     }
