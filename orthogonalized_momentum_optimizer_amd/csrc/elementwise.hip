@@ -145,8 +145,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
         }
       }
     }
-    ss += (u[0] * u[0] + u[1] * u[1]) + (u[2] * u[2] + u[3] * u[3]);
     if (!L.tall) {
+      ss += (u[0] * u[0] + u[1] * u[1]) + (u[2] * u[2] + u[3] * u[3]);
       store4<XDT>(x, xidx<XDT>(r, c, L.np), u);  // wide (i, j) = (r, c); r < mp, c < np
     } else {
 #pragma unroll
@@ -156,6 +156,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
 
   if (L.tall) {
     __syncthreads();
+    // the sum of squares is taken over the wide form, element for element in the order of
+    // the wide path, so a matrix and its transpose give bitwise the same partial sums
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int a = (t >> 4) + 16 * k;  // wide row (original column) within the tile
@@ -163,6 +165,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = tile[b + e][a];
+      ss += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
       store4<XDT>(x, xidx<XDT>(c0 + a, r0 + b, L.np), v);
     }
   }

@@ -236,6 +236,32 @@ def test_transpose_path_matches_wide_bitwise():
     assert np.array_equal(outs[0], outs[1].T)
 
 
+def test_step_on_transpose_is_transpose_bitwise():
+    """A whole Muon step on (W^T, G^T) gives bitwise the transposes of W, M and O from the step
+    on (W, G): momentum and update are elementwise, the wide form X0 and the sum of squares
+    behind the norm are formed in the same order on both paths. Column counts cover the
+    8-wide, the 4-wide and the per-element access paths."""
+    _announce("step on the transpose")
+    dev = torch.device("cuda", 0)
+    for r, c in ((320, 192), (200, 68), (130, 37)):
+        wl = si.custom([(r, c)], dtype="bf16", steps=2, cfg_id=119)
+        W0, grads = si.weight(wl, 0), [si.grad(wl, 0, t) for t in range(2)]
+        res = []
+        for tr in (False, True):
+            f = (lambda x: x.t().contiguous()) if tr else (lambda x: x)
+            W = f(W0).to(dev)
+            M = torch.zeros(W.shape, dtype=torch.float32, device=dev)
+            O = torch.empty(W.shape, dtype=torch.float32, device=dev)
+            plan = MuonPlan([W.shape], [W.dtype], [W.dtype], "bf16", dev)
+            for t in range(2):
+                plan.step([W], [f(grads[t]).to(dev)], [M], make_config(), outs=[O])
+            torch.cuda.synchronize()
+            plan.close()
+            res.append([f64(x) for x in (W, M, O)])
+        for a, b in zip(res[0], res[1]):
+            assert np.array_equal(a, b.T), (r, c)
+
+
 def test_newton_schulz_entry_against_oracle():
     _announce("newton_schulz entry")
     dev = torch.device("cuda", 0)
