@@ -156,9 +156,11 @@ int muon_newton_schulz(muon_plan *plan, const void *const *in, void *const *out,
 void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
 
 /* Kernel timing for measurement. When enabled, every later muon_step/muon_newton_schulz
- * records a HIP event pair around each kernel launch on the call's stream (events are
- * created here, on the current device; the step itself still allocates nothing). Enabling
- * resets the totals; disabling releases the events. */
+ * times each kernel launch with a HIP event pair that the launch itself updates with the
+ * kernel's start and end (hipExtLaunchKernel; no marker packets are added to the stream).
+ * Events are created here, on the current device; the step itself still allocates nothing.
+ * Enabling resets the totals; disabling releases the events. Not for use while the call's
+ * stream is being captured into a graph: capture the step with profiling disabled. */
 int muon_plan_set_profiling(muon_plan *plan, int enable);
 
 /* Kinds of kernel, in the order of a step. */
