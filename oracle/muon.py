@@ -11,8 +11,10 @@ The step, per matrix (W: weights, M: momentum buffer, G: gradient):
    nu = ||U||_F;  X = U / (nu + eps).
 3. Wide form: if rows > cols, X <- X^T (the iteration of step 4 commutes with
    transposition, so this changes nothing in exact arithmetic).
-4. Quintic Newton-Schulz [P3 "Newton-Schulz正交化"], repeated ns_steps times with
-   (a, b, c) = (3.4445, -4.7750, 2.0315):  A = X X^T;  B = b A + c A A;  X = a X + B X.
+4. Quintic Newton-Schulz [P3 "Newton-Schulz正交化"], ns_steps rounds with
+   (a, b, c) = (3.4445, -4.7750, 2.0315). A round is the odd quintic p(s) = a s + b s^3 +
+   c s^5 applied to every singular value of X: X <- a X + b (X X^T) X + c (X X^T)^2 X,
+   evaluated here as q(X X^T) X with q(t) = a + t (b + c t) (Horner's rule).
 5. Back to the original orientation: O = X (or X^T if step 3 transposed).
 6. Parameter update [P3 "核心算法", third phase of ``step``]:  W <- W - lr * O.
 
@@ -59,16 +61,22 @@ def frobenius_normalize(U: np.ndarray, eps: float = DEFAULT_EPS) -> Tuple[np.nda
 
 def newton_schulz(X: np.ndarray, steps: int, abc: Sequence[float] = DEFAULT_ABC,
                   schedule: Sequence[Sequence[float]] | None = None) -> np.ndarray:
-    """[P3 "Newton-Schulz正交化"] ``steps`` rounds of A = X X^T, B = bA + cA^2, X = aX + BX.
+    """[P3 "Newton-Schulz正交化"] ``steps`` rounds of the quintic map on X.
+
+    One round maps X = U S V^T to U p(S) V^T with p(s) = a s + b s^3 + c s^5, the odd
+    quintic whose coefficients the page prints. Because X X^T = U S^2 U^T, that is
+    p(X) = q(X X^T) X with q(t) = a + b t + c t^2, and q of the m x m Gram matrix is
+    formed by Horner's rule, q(G) = a I + G (b I + c G), then applied to X.
 
     ``X`` is used as given (no transposition, no normalisation). ``schedule``, if given,
     holds one (a, b, c) triple per round in place of the fixed ``abc``."""
     X = np.array(X, dtype=np.float64, copy=True)
+    eye = np.eye(X.shape[0])
     for k in range(steps):
         a, b, c = schedule[k] if schedule is not None else abc
-        A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
+        gram = X @ X.T                                  # X X^T, the Gram matrix
+        q_of_gram = a * eye + gram @ (b * eye + c * gram)   # q(X X^T), Horner's rule
+        X = q_of_gram @ X
     return X
 
 

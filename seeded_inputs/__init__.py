@@ -132,19 +132,32 @@ def weight(wl: Workload, index: int):
     return _to_stored(x, wl.dtype)
 
 
+def _grad_rng(wl: Workload, index: int, step: int) -> np.random.Generator:
+    return rng(wl.cfg_id, KIND_GRAD, index, 0 if wl.reuse_grad else step)
+
+
 def grad(wl: Workload, index: int, step: int):
     """Gradient of matrix ``index`` at step ``step`` (0-based) as a CPU torch tensor."""
     r, c = wl.shapes[index]
-    g = rng(wl.cfg_id, KIND_GRAD, index, 0 if wl.reuse_grad else step)
+    g = _grad_rng(wl, index, step)
     if wl.iid_t3_entries:
         x = wl.grad_std * g.standard_t(3, size=(r, c))
     elif wl.heavy_tailed_rows:
-        t = g.standard_t(3, size=(r, 1))
+        t = g.standard_t(3, size=(r, 1))   # the row scales: drawn first (heavy_row_scales)
         z = g.standard_normal(size=(r, c))
         x = wl.grad_std * np.abs(t) * z
     else:
         x = g.normal(0.0, wl.grad_std, size=(r, c))
     return _to_stored(x, wl.dtype)
+
+
+def heavy_row_scales(wl: Workload, index: int, step: int) -> np.ndarray:
+    """|t_i|, the Student-t(3) row scales of a heavy-tailed-rows gradient (rows of matrix
+    ``index`` at ``step``), as ``grad`` draws them (its generator's first draw)."""
+    if not wl.heavy_tailed_rows:
+        raise ValueError(f"{wl.name} has no heavy-tailed rows")
+    r, _ = wl.shapes[index]
+    return np.abs(_grad_rng(wl, index, step).standard_t(3, size=(r, 1))[:, 0])
 
 
 def custom(shapes, dtype: str = "bf16", steps: int = 1, grad_std: float = 1e-3,

@@ -2,7 +2,8 @@
 compiled gfx950 assembly is checked statically (no GPU needed, hipcc cross-compiles)."""
 import pytest
 
-from orthogonalized_momentum_optimizer_amd import asm_check, build
+import asm_check
+from orthogonalized_momentum_optimizer_amd import build
 
 KERNEL_SOURCES = ["ns_apply_bf16.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip"]
 
@@ -40,6 +41,101 @@ def test_checker_honours_partial_waits():
     ])
     v = asm_check.violations(text)
     assert len(v) == 1 and "v21" in v[0]
+
+
+def test_checker_follows_a_read_across_a_branch_join():
+    """A read issued before a conditional branch is still pending where the paths join: a
+    copy there, before the wait, is flagged (a checker that forgets pending reads at labels
+    would miss it)."""
+    text = "\n".join([
+        "ds_read_b128 v[4:7], v0 offset:0",
+        "s_cbranch_scc1 .LBB0_2",
+        "v_mov_b32_e32 v9, v1",
+        ".LBB0_2:",
+        "v_mov_b32_e32 v20, v4",
+        "s_waitcnt lgkmcnt(0)",
+        "s_endpgm",
+    ])
+    v = asm_check.violations(text)
+    assert len(v) == 1 and "v20, v4" in v[0]
+
+
+def test_checker_flags_a_read_issued_on_one_path_only():
+    """The shape of the bug once found in a kernel: a transposing read issued on one path
+    only, its result copied at the join before the wait."""
+    text = "\n".join([
+        "s_cbranch_scc0 .LBB0_3",
+        "ds_read_b64_tr_b16 v[8:9], v2",
+        ".LBB0_3:",
+        "v_mov_b32_e32 v30, v8",
+        "s_waitcnt lgkmcnt(0)",
+        "v_mov_b32_e32 v31, v9",
+        "s_endpgm",
+    ])
+    v = asm_check.violations(text)
+    assert len(v) == 1 and "v30, v8" in v[0]
+
+
+def test_checker_flags_a_wait_taken_on_one_path_only():
+    text = "\n".join([
+        "ds_read_b128 v[4:7], v0",
+        "s_cbranch_scc1 .LBB0_2",
+        "s_waitcnt lgkmcnt(0)",
+        ".LBB0_2:",
+        "v_add_f32_e32 v20, v4, v5",
+        "s_endpgm",
+    ])
+    assert len(asm_check.violations(text)) == 1
+
+
+def test_checker_follows_a_loop_back_edge():
+    """A read issued at the end of a loop body reaches the top of the loop pending."""
+    text = "\n".join([
+        "ds_read_b128 v[4:7], v0",
+        "s_waitcnt lgkmcnt(0)",
+        ".LBB0_1:",
+        "v_mov_b32_e32 v20, v4",
+        "ds_read_b128 v[4:7], v0 offset:64",
+        "s_cbranch_scc1 .LBB0_1",
+        "s_waitcnt lgkmcnt(0)",
+        "s_endpgm",
+    ])
+    v = asm_check.violations(text)
+    assert len(v) >= 1 and "v20, v4" in v[0]
+
+
+def test_checker_accepts_waits_on_every_path():
+    text = "\n".join([
+        "ds_read_b128 v[4:7], v0",
+        "s_cbranch_scc1 .LBB0_2",
+        "s_waitcnt lgkmcnt(0)",
+        "v_mov_b32_e32 v9, v4",
+        "s_branch .LBB0_3",
+        ".LBB0_2:",
+        "ds_read_b128 v[12:15], v1",
+        "s_waitcnt lgkmcnt(1)",
+        ".LBB0_3:",
+        "v_mov_b32_e32 v20, v4",
+        "s_waitcnt lgkmcnt(0)",
+        "v_mov_b32_e32 v21, v12",
+        "s_endpgm",
+    ])
+    assert asm_check.violations(text) == []
+
+
+def test_checker_completes_scalar_loads_only_at_zero():
+    """Scalar loads may complete out of order: a partial wait does not cover them."""
+    text = "\n".join([
+        "s_load_dword s4, s[0:1], 0x0",
+        "ds_read_b32 v4, v0",
+        "s_waitcnt lgkmcnt(1)",
+        "s_mov_b32 s5, s4",
+        "s_waitcnt lgkmcnt(0)",
+        "s_mov_b32 s6, s4",
+        "s_endpgm",
+    ])
+    v = asm_check.violations(text)
+    assert len(v) == 1 and "s5, s4" in v[0]
 
 
 def _vm_sequence(func_text):

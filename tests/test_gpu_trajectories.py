@@ -1,0 +1,102 @@
+"""GPU parity over the workloads' whole trajectories: every step of every watched matrix is
+compared with the oracle, at full size, in the launch configuration bench.py times (all
+matrices of the workload in one plan, one call per step).
+
+The oracle advances each watched matrix from its own state (float64 W and M from the same
+initial weights and the same gradients), so rounding drift of the GPU's bf16-stored weights
+over 10 or 20 steps is inside what is compared. Gates are those of ``harness``: O <= 3e-2
+(bf16 rounds) / 1e-4 (fp32 rounds), M <= 1e-6, W <= 3e-2 against the exact trajectory and,
+in the fp32 rounds, against the trajectory as bf16 storage leaves it at a derived bound.
+
+What is watched (matrices are independent of each other, checked bitwise elsewhere):
+
+* attn_768 (1 x 768x768, 10 steps): the matrix, both precisions.
+* gpt2_124m (72 matrices, 20 steps): bf16: the first, middle and last matrix of each shape
+  (9 matrices); fp32: one matrix of each shape.
+* tall_stress (96 matrices, 20 steps): bf16: the first, middle and last of each shape, plus
+  the tall and the wide matrix whose step-0 gradient has the most row-dominated energy (one
+  row holds 57% of it in the wide one); fp32: the two outliers.
+* gpt2_1p5b (288 matrices, 10 steps): bf16: all six matrices of layers 0, 24 and 47, one
+  layer per test; fp32: 4 steps of one matrix of each shape in layers 0 and 47.
+"""
+import pytest
+
+import seeded_inputs as si
+from harness import run_lockstep
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _row_outliers(wl):
+    """The tall and the wide matrix whose step-0 gradient has the largest share of its
+    energy in one row."""
+    best = {}
+    for i, (r, c) in enumerate(wl.shapes):
+        t2 = si.heavy_row_scales(wl, i, 0) ** 2
+        share = float(t2.max() / t2.sum())
+        key = r > c
+        if key not in best or share > best[key][1]:
+            best[key] = (i, share)
+    return sorted(i for i, _ in best.values())
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_attn_768_trajectory(precision):
+    wl = si.WORKLOADS["attn_768"]
+    _announce(f"attn_768 {precision}, {wl.steps} steps")
+    run_lockstep(wl, wl.steps, precision, watch=[0])
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_124m_trajectory_bf16():
+    wl = si.WORKLOADS["gpt2_124m"]
+    watch = si.sample_indices(wl)
+    _announce(f"gpt2_124m bf16, {wl.steps} steps, watch {watch}")
+    run_lockstep(wl, wl.steps, "bf16", watch)
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_124m_trajectory_f32():
+    wl = si.WORKLOADS["gpt2_124m"]
+    watch = [0, 4, 5]
+    _announce(f"gpt2_124m f32 debug rounds, {wl.steps} steps, watch {watch}")
+    run_lockstep(wl, wl.steps, "f32", watch)
+
+
+@pytest.mark.timeout(600)
+def test_tall_stress_trajectory_bf16():
+    wl = si.WORKLOADS["tall_stress"]
+    watch = sorted(set(si.sample_indices(wl)) | set(_row_outliers(wl)))
+    _announce(f"tall_stress bf16, {wl.steps} steps, watch {watch}")
+    run_lockstep(wl, wl.steps, "bf16", watch)
+
+
+@pytest.mark.timeout(600)
+def test_tall_stress_trajectory_f32():
+    wl = si.WORKLOADS["tall_stress"]
+    watch = _row_outliers(wl)
+    _announce(f"tall_stress f32 debug rounds, {wl.steps} steps, watch {watch}")
+    run_lockstep(wl, wl.steps, "f32", watch)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("layer", [0, 24, 47])
+def test_gpt2_1p5b_trajectory_bf16(layer):
+    wl = si.WORKLOADS["gpt2_1p5b"]
+    watch = list(range(6 * layer, 6 * layer + 6))
+    _announce(f"gpt2_1p5b bf16, {wl.steps} steps, layer {layer}: watch {watch}")
+    run_lockstep(wl, wl.steps, "bf16", watch, gpu_fill_others=True)
+
+
+@pytest.mark.timeout(900)
+def test_gpt2_1p5b_trajectory_f32():
+    wl = si.WORKLOADS["gpt2_1p5b"]
+    watch = [0, 4, 5, 6 * 47, 6 * 47 + 4, 6 * 47 + 5]
+    _announce(f"gpt2_1p5b f32 debug rounds, 4 steps, watch {watch}")
+    run_lockstep(wl, 4, "f32", watch, gpu_fill_others=True)
+

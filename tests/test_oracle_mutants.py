@@ -12,8 +12,10 @@ import pins
 
 
 def _ns_factory(kind):
+    """The oracle's round X <- q(X X^T) X, q(t) = a + t (b + c t), with one mistake."""
     def ns(X, steps, abc=om.DEFAULT_ABC, schedule=None):
         X = np.array(X, dtype=np.float64, copy=True)
+        eye = np.eye(X.shape[0])
         n_rounds = steps + 1 if kind == "extra_round" else steps
         for k in range(n_rounds):
             a, b, c = schedule[k] if schedule is not None and k < len(schedule) else abc
@@ -21,17 +23,16 @@ def _ns_factory(kind):
                 b, c = c, b
             if kind == "sign_b":
                 b = -b
-            A = X.T @ X if kind == "gram_transposed" else X @ X.T
-            if A.shape[0] != X.shape[0]:          # X^T X only composes for square X
-                A = X @ X.T + 1e-3
-            if kind == "linear_c":
-                B = b * A + c * A
+            gram = X.T @ X if kind == "gram_transposed" else X @ X.T
+            if gram.shape[0] != X.shape[0]:       # X^T X only composes for square X
+                gram = X @ X.T + 1e-3
+            if kind == "linear_c":                # c t in place of c t^2
+                q = a * eye + gram * (b + c)
             else:
-                B = b * A + c * (A @ A)
+                q = a * eye + gram @ (b * eye + c * gram)
             if kind == "drop_aX":
-                X = B @ X
-            else:
-                X = a * X + B @ X
+                q = q - a * eye
+            X = q @ X
         return X
     return ns
 
