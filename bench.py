@@ -169,26 +169,33 @@ def cpu_baseline(wl, budget_s=12.0):
                     break
     except OSError:
         pass
-    t0 = time.perf_counter()
+    # only the oracle's own calls are timed: each matrix's inputs are drawn (and upcast to
+    # float64, as the oracle does first) before its clock starts
+    elapsed, gen_s = 0.0, 0.0
     done_flops, used = 0.0, 0
     for i, (r, c) in enumerate(wl.shapes):
-        W, G = si.weight(wl, i), si.grad(wl, i, 0)
-        oracle.muon_step(W, np.zeros((r, c)), G)
+        g0 = time.perf_counter()
+        W = si.weight(wl, i).double().numpy()
+        G = si.grad(wl, i, 0).double().numpy()
+        M = np.zeros((r, c))
+        t0 = time.perf_counter()
+        gen_s += t0 - g0
+        oracle.muon_step(W, M, G)
+        elapsed += time.perf_counter() - t0
         m, n = min(r, c), max(r, c)
         done_flops += 5 * (4.0 * m * m * n + 2.0 * m ** 3)
         used = i + 1
-        if time.perf_counter() - t0 > budget_s:
+        if elapsed > budget_s:
             break
-    elapsed = time.perf_counter() - t0
     frac = done_flops / wl.ns_flops_per_step()
     sec_per_step = elapsed / frac
     return {"value": 1.0 / sec_per_step, "unit": "Muon steps/s", "cores": cores,
             "kind": "oracle", "blas": blas, "cpu_model": cpu_model,
             "host_cpus": os.cpu_count(),
             "sample": f"float64 oracle, one step of matrices 0..{used - 1} of {wl.name} "
-                      f"({used}/{wl.n} matrices, {frac * 100:.1f}% of the step's nominal flops,"
-                      f" input generation included), scaled to the full step by flops; "
-                      f"{elapsed:.1f} s"}
+                      f"({used}/{wl.n} matrices, {frac * 100:.1f}% of the step's nominal flops),"
+                      f" scaled to the full step by flops; {elapsed:.1f} s in the oracle "
+                      f"(input generation, {gen_s:.1f} s, not timed)"}
 
 
 def adam_bytes_per_element(pdt="bf16", gdt="bf16"):
@@ -398,6 +405,10 @@ def main():
         stop.record(stream)
         torch.cuda.synchronize()
         out["ms_per_step_profiled_pass"] = start.elapsed_time(stop) / args.steps
+        out["profiled_pass_note"] = (
+            "kernel durations come from the per-launch HIP events of this second pass; the "
+            "events make the pass itself slower per step (ms_per_step_profiled_pass against "
+            "ms_per_step) but each duration spans its own kernel only")
         prof = plan.read_profile()
         plan.set_profiling(False)
         kernels = {}
@@ -410,6 +421,15 @@ def main():
         out["ns_tflops_kernels"] = ns_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
         peak_mm = PEAK_BF16_TFLOPS if args.precision == "bf16" else PEAK_F32_TFLOPS
         out["ns_frac_of_peak"] = (out["ns_tflops_kernels"] or 0) / peak_mm
+        # the step's roofline: the nominal Newton-Schulz flops at the bf16 peak plus the
+        # elementwise kernels' algorithmic bytes (read G, read and write M and W) at the HBM
+        # peak, over the measured step time
+        ew_bytes = work["momentum"] + work["update"]
+        ns_ms = ns_flops / (peak_mm * 1e12) * 1e3
+        ew_ms = ew_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+        out["step_roofline"] = {"ns_ms_at_peak": ns_ms, "elementwise_ms_at_peak": ew_ms,
+                                "elementwise_bytes": ew_bytes, "step_ms": ms,
+                                "frac": (ns_ms + ew_ms) / ms}
         dom = max(prof, key=lambda k: prof[k][0])
         dms, dl = prof[dom]
         if dom in ("gram", "poly", "apply"):

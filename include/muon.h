@@ -31,6 +31,13 @@
  *   D_ij = O_ij / (sqrt(v_i) + row_eps)
  *   O   <- D * ||O||_F / ||D||_F                     (total energy kept; 0 stays 0)
  *
+ * Range: every finite fp32 value of U is supported. The norm is summed in double, and a
+ * matrix whose ||U||_F lies outside [2^-40, 2^40] has its copy in the iteration's workspace
+ * scaled by an exact power of two before the first product, with the inverse power folded
+ * into 1/(||U||_F + eps); the fp32 accumulation of the products then neither overflows nor
+ * underflows. (The rescale is one extra pass over that matrix, taken only for such inputs.)
+ * Products whose fp32 value is subnormal (below 2^-126) may be flushed to zero.
+ *
  * Conventions shared by every entry point:
  *   - All buffers are device memory on the current HIP device, row-major, contiguous, with
  *     16-byte aligned base addresses. The caller owns every buffer.

@@ -84,13 +84,21 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Sum of the squares of four fp32 values in double: each square is exact in double (24-bit
+// significands give at most 48 bits), so the per-tile sums neither overflow nor underflow
+// for any finite fp32 input, and the order of the additions is fixed.
+__device__ __forceinline__ double sumsq4(const float v[4]) {
+  const double a = v[0], b = v[1], c = v[2], d = v[3];
+  return (a * a + b * b) + (c * c + d * d);
+}
+
 // One 64x64 tile of the padded wide form X (mp x np) per block, matrix q = blockIdx.y.
-// Momentum (in place), U, the tile's sum of U^2, and X0 = U stored in the wide form; padding
-// positions of X0 receive zeros. GDT: grad dtype, XDT: X dtype (0 bf16, 1 f32).
+// Momentum (in place), U, the tile's sum of U^2 (in double), and X0 = U stored in the wide
+// form; padding positions of X0 receive zeros. GDT: grad dtype, XDT: X dtype (0 bf16, 1 f32).
 template <int GDT, int XDT>
 __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
   __shared__ float tile[kTile][kTile + 1];
-  __shared__ float red[4];
+  __shared__ double red[4];
   const int q = blockIdx.y;
   const int t = threadIdx.x;
   const int tiles_n = L.np / kTile;
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
   void* x = static_cast<char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
   const float beta = L.beta;
   const int lc = 4 * (t & 15);
-  float ss = 0.f;
+  double ss = 0.0;
 
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
       }
     }
     if (!L.tall) {
-      ss += (u[0] * u[0] + u[1] * u[1]) + (u[2] * u[2] + u[3] * u[3]);
+      ss += sumsq4(u);
       store4<XDT>(x, xidx<XDT>(r, c, L.np), u);  // wide (i, j) = (r, c); r < mp, c < np
     } else {
 #pragma unroll
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = tile[b + e][a];
-      ss += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
+      ss += sumsq4(v);
       store4<XDT>(x, xidx<XDT>(c0 + a, r0 + b, L.np), v);
     }
   }
@@ -179,25 +187,68 @@ __global__ __launch_bounds__(256) void momentum_kernel(ElemLaunch L) {
   }
 }
 
-// One block per matrix: nu = sqrt(sum of tile partials) in double, in a fixed order.
-__global__ __launch_bounds__(256) void norm_kernel(const float* partials, int tiles,
-                                                   float* scales, float eps) {
+// One block per matrix: nu = sqrt(sum of tile partials) in double, in a fixed order, and the
+// scales s1 = 1/(nu + eps), s2 = s1^2 that the first round folds into its products.
+//
+// X0 holds U itself (unnormalised), and the first round's Gram product accumulates the
+// products of its entries in fp32: entries near fp32's range limits would overflow (|U| of
+// about 1e17 and more) or underflow (squares below 2^-126) there before s2 is applied. A
+// matrix whose nu lies outside [2^-40, 2^40] therefore has its X0 rescaled here by the exact
+// power of two 2^-k, k = floor(log2 nu) (so its entries are below 2 in magnitude), and
+// s1 = 2^k / (nu + eps): X0 s1 is the same U / (nu + eps). Inside that range nothing is
+// rescaled (every Gram entry and partial product then lies between 2^-110 and 2^95, for any
+// K up to 2^15); the rescale is one block's pass over the matrix, taken only for such inputs.
+__global__ __launch_bounds__(256) void norm_kernel(const double* partials, int tiles,
+                                                   float* scales, float eps, void* x0,
+                                                   size_t mn, int x_f32) {
   __shared__ double red[4];
+  __shared__ int kexp;
   const int q = blockIdx.x, t = threadIdx.x;
-  const float* p = partials + (size_t)q * tiles;
+  const double* p = partials + (size_t)q * tiles;
   double s = 0.0;
-  for (int i = t; i < tiles; i += 256) s += (double)p[i];
+  for (int i = t; i < tiles; i += 256) s += p[i];
   s = wave_sum(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
   if (t == 0) {
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);
     const double nu = sqrt(tot);
-    const double s1 = 1.0 / (nu + (double)eps);
+    int k = 0;
+    if (nu > 0.0 && nu <= 1.7976931348623157e308 && (nu < 0x1p-40 || nu > 0x1p40))
+      k = ilogb(nu);  // nu 2^-k in [1, 2); |k| >= 40 here
+    const double s1 = ldexp(1.0, k) / (nu + (double)eps);
     scales[4 * q + 0] = (float)s1;
     scales[4 * q + 1] = (float)(s1 * s1);
     scales[4 * q + 2] = (float)nu;
     scales[4 * q + 3] = 0.f;
+    kexp = k;
+  }
+  __syncthreads();
+  const int k = kexp;
+  if (k == 0) return;
+  // X0 <- X0 2^-k, exact (the results are representable: their magnitudes are below 2)
+  const double f = ldexp(1.0, -k);
+  if (x_f32) {
+    float4* x = reinterpret_cast<float4*>(static_cast<float*>(x0) + (size_t)q * mn);
+    for (size_t i = t; i < mn / 4; i += 256) {
+      float4 v = x[i];
+      v.x = (float)(v.x * f); v.y = (float)(v.y * f);
+      v.z = (float)(v.z * f); v.w = (float)(v.w * f);
+      x[i] = v;
+    }
+  } else {
+    uint4* x = reinterpret_cast<uint4*>(static_cast<uint16_t*>(x0) + (size_t)q * mn);
+    for (size_t i = t; i < mn / 8; i += 256) {
+      uint4 w = x[i];
+      uint32_t* h = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = (float)(bf16_bits_to_f32(h[e] & 0xffffu) * f);
+        const float hi = (float)(bf16_bits_to_f32(h[e] >> 16) * f);
+        h[e] = pack_bf16(lo, hi);
+      }
+      x[i] = w;
+    }
   }
 }
 
@@ -462,9 +513,10 @@ hipError_t launch_momentum(const ElemLaunch& L, int grad_dt, int x_f32, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_norm(const float* partials, int tiles, float* scales, int count, float eps,
-                       hipStream_t s) {
-  launch_k(norm_kernel, dim3(count), dim3(256), 0, s, partials, tiles, scales, eps);
+hipError_t launch_norm(const double* partials, int tiles, float* scales, int count, float eps,
+                       void* x0, size_t mn, int x_f32, hipStream_t s) {
+  launch_k(norm_kernel, dim3(count), dim3(256), 0, s, partials, tiles, scales, eps, x0, mn,
+           x_f32);
   return hipGetLastError();
 }
 

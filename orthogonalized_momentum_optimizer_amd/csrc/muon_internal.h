@@ -55,7 +55,7 @@ struct ElemLaunch {
   int mp, np;                      // padded wide shape (X is mp x np)
   int vec;                         // cols % 4 == 0: 4-wide vector access along rows
   void* x;                         // X buffer of slot0 (bf16 or f32), slot stride mp*np
-  float* partials;                 // K1: per-tile sums of squares of slot0
+  double* partials;                // K1: per-tile sums of squares of slot0
   const float* scales;             // per-slot {s1, s2, nu, 0} of slot0
   float beta;
   int nesterov;
@@ -78,9 +78,11 @@ hipError_t launch_update(const ElemLaunch& L, int param_dt, int out_param_dt, in
 // factors gamma / (sqrt(v_i) + eps) that the update kernel applies to O.
 hipError_t launch_rowstat(const ElemLaunch& L, int x_f32, hipStream_t s);
 hipError_t launch_roweq_finish(const ElemLaunch& L, hipStream_t s);
-// Per-matrix norm finish: scales[4*i] = 1/(nu+eps), [4*i+1] = that squared, [4*i+2] = nu.
-hipError_t launch_norm(const float* partials, int tiles_per_mat, float* scales, int count,
-                       float eps, hipStream_t s);
+// Per-matrix norm finish: scales[4*i] = s1 = 1/(nu+eps), [4*i+1] = s1^2, [4*i+2] = nu. A
+// matrix with nu outside [2^-40, 2^40] has its X0 (count matrices of mn elements at x0,
+// bf16 or fp32) scaled in place by 2^-floor(log2 nu), and s1 = 2^floor(log2 nu) / (nu+eps).
+hipError_t launch_norm(const double* partials, int tiles_per_mat, float* scales, int count,
+                       float eps, void* x0, size_t mn, int x_f32, hipStream_t s);
 
 // One batched Newton-Schulz product over a group of `batch` padded mp x np matrices.
 struct NsGroup {

@@ -218,15 +218,24 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     const int i = m >> 2, j = m & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
   };
-  // Waits for this wave's loads of the next stage, then the block barrier: that stage is
-  // complete for every wave. `later` counts the loads issued after it; any vector-memory
-  // operation issued in between (the previous tile's output stores) only makes the wait
-  // longer, never too short: the counter completes in issue order.
-  auto stage_ready = [&](int later) {
-    if (later >= 3) vm_wait<3 * kLoadsPerStage>();
-    else if (later == 2) vm_wait<2 * kLoadsPerStage>();
-    else if (later == 1) vm_wait<kLoadsPerStage>();
-    else vm_wait<0>();
+  // Waits for this wave's loads of a stage, then the block barrier: that stage is complete
+  // for every wave. The vector-memory counter completes loads and stores in issue order, so
+  // the wait leaves pending exactly the operations issued after the stage's loads: `later`
+  // stages of loads, plus `stores` output stores when the stage is one of a tile's first
+  // four, which were prefetched before the previous tile's epilogue stored its output (32
+  // per wave, 16 when the tile's right half lies outside the matrix, 0 when the wave's rows
+  // do; `stores` is wave-uniform).
+  auto wait_n = [&](auto n_t, int stores) {
+    constexpr int n = decltype(n_t)::value;
+    if (stores == 32) vm_wait<n + 32>();
+    else if (stores == 16) vm_wait<n + 16>();
+    else vm_wait<n>();
+  };
+  auto stage_ready = [&](int later, int stores) {
+    if (later >= 3) wait_n(std::integral_constant<int, 3 * kLoadsPerStage>{}, stores);
+    else if (later == 2) wait_n(std::integral_constant<int, 2 * kLoadsPerStage>{}, stores);
+    else if (later == 1) wait_n(std::integral_constant<int, kLoadsPerStage>{}, stores);
+    else wait_n(std::integral_constant<int, 0>{}, stores);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
   };
@@ -241,6 +250,7 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   Frags f0, f1;
   Tile cur;
+  int stores = 0;  // output stores of the previous tile issued after this tile's prefetch
   auto iteration = [&](int kt, auto refill_t, auto more_t) {
     constexpr bool refill = decltype(refill_t)::value, more = decltype(more_t)::value;
     const uint32_t cb = stage_base(kt);
@@ -255,8 +265,9 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     });
     ready(f1, a1, b1);  // slice 1 is in registers: this wave is done reading stage kt
     if constexpr (more) {
-      if constexpr (refill) stage_ready(NSTAGE - 2);
-      else stage_ready(min(NSTAGE - 2, KT - 2 - kt));
+      const int st = kt + 1 < NSTAGE ? stores : 0;  // stage kt + 1 was prefetched
+      if constexpr (refill) stage_ready(NSTAGE - 2, st);
+      else stage_ready(min(NSTAGE - 2, KT - 2 - kt), st);
     }
     const uint32_t nxt = stage_base(kt + 1);
     const uint32_t va0n = nxt + aoff0, vbn = nxt + boff;
@@ -288,7 +299,7 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    stage_ready(NSTAGE - 1);
+    stage_ready(NSTAGE - 1, stores);
     static_for<12>([&](auto OP) { lds_op<0, decltype(OP)::value>(lds0 + aoff0, lds0 + boff, f0); });
     ready(f0, a0, b0);
 
@@ -326,6 +337,7 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     // padded matrix or wholly outside.
     const int half = lane >> 5;
     const bool rows_in = row0 + wr * 128 < g.mp, right_in = col0 + 128 < np;
+    stores = rows_in ? (right_in ? 32 : 16) : 0;  // the stores issued below
     char* const seg0 = reinterpret_cast<char*>(
         out + toff(min(row0 + wr * 128 + (lane & 31), g.mp - 1), col0 + 32 * wc + 8 * half, np));
     {

@@ -219,7 +219,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
 
   // phase 1: momentum, norm partials, X0; then the norms
   auto momentum_and_norm = [&](const Group& G) {
-    float* part = reinterpret_cast<float*>(base + G.off_part);
+    double* part = reinterpret_cast<double*>(base + G.off_part);
     for (int si : G.sets) {
       const LaunchSet& S = p->sets[si];
       for (size_t q0 = 0; q0 < S.mats.size(); q0 += kMaxPerLaunch) {
@@ -246,7 +246,8 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
       }
     }
     L.run(MUON_KERNEL_NORM, "norm", [&] {
-      return launch_norm(part, G.tiles64, scales_of(G), G.count, cfg->eps, stream);
+      return launch_norm(part, G.tiles64, scales_of(G), G.count, cfg->eps, base + G.off_x0,
+                         (size_t)G.mp * G.np, f32 ? 1 : 0, stream);
     });
   };
 
@@ -471,7 +472,7 @@ int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
     G.off_x1 = off; off = align256(off + xs);
     G.off_a = off; off = align256(off + as);
     G.off_b = off; off = align256(off + as);
-    G.off_part = off; off = align256(off + (size_t)G.count * G.tiles64 * 4);
+    G.off_part = off; off = align256(off + (size_t)G.count * G.tiles64 * 8);
     G.off_scales = off; off = align256(off + (size_t)G.count * 16);
     G.off_rowsum = off; off = align256(off + (size_t)G.count * kRowParts * G.np * 4);
     G.off_rowf = off; off = align256(off + (size_t)G.count * G.np * 4);

@@ -58,7 +58,7 @@ def test_status_strings():
 
 def _ws_expected(shapes, esz):
     """Workspace layout: per padded wide group X0, X1 (count*mp*np), A, B (count*mp*mp),
-    partial sums (count * 64x64 tiles of X), scales (16 B per matrix), partial row sums and
+    partial sums (count * 64x64 tiles of X, doubles), scales (16 B per matrix), partial row sums and
     row factors of the row equaliser (count*8*np and count*np floats), each 256-aligned."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     groups = {}
@@ -72,7 +72,7 @@ def _ws_expected(shapes, esz):
         tot = al(tot + cnt * mp * np_ * esz)
         tot = al(tot + cnt * mp * mp * esz)
         tot = al(tot + cnt * mp * mp * esz)
-        tot = al(tot + cnt * (mp // 64) * (np_ // 64) * 4)
+        tot = al(tot + cnt * (mp // 64) * (np_ // 64) * 8)
         tot = al(tot + cnt * 16)
         tot = al(tot + cnt * 8 * np_ * 4)
         tot = al(tot + cnt * np_ * 4)

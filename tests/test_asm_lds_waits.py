@@ -189,3 +189,28 @@ def test_poly_b_a_loads_match_the_tail_waits():
     # the Gram kernels load no b A term
     gram = [f for f in funcs if f.startswith("_ZN4muon12_GLOBAL__N_111ns_sym_bf16ILi0")]
     assert gram and all("P" not in _vm_sequence(f) for f in gram)
+
+
+def test_apply_tile_start_waits_count_the_previous_stores():
+    """The persistent apply kernels prefetch a tile's first four stages before the previous
+    tile's epilogue stores its output (32 stores per wave, 16 when the tile's right half lies
+    outside the matrix, none when the wave's rows do). The vector-memory counter completes in
+    issue order, so the wait for the new tile's first stage leaves 3 stages of loads plus
+    those stores pending: the compiled kernels must hold the three variants 24, 40 and 56,
+    with 32 conditional stores and the 32-load prefetch before them."""
+    import re
+    try:
+        path = build.device_asm("ns_apply_bf16.hip")
+    except RuntimeError as e:
+        pytest.skip(str(e))
+    text = open(path).read()
+    funcs = re.split(r"\n(?=_Z\S+: ; @)", text)
+    persistent = [f for f in funcs if re.match(r"_ZN4muon12_GLOBAL__N_1\d+ns_apply_bf16", f)]
+    assert len(persistent) == 4, [f.split(":")[0] for f in persistent]
+    for f in persistent:
+        waits = [int(x) for x in re.findall(r"s_waitcnt[^\n]*vmcnt\((\d+)\)", f)]
+        assert {24, 40, 56} <= set(waits) and max(waits) == 56, sorted(set(waits))
+        assert len(re.findall(r"\n\s*global_store_dwordx4", f)) == 32
+        body = "\n".join(ln.strip() for ln in f.splitlines())
+        last_prefetch = body.rfind("global_load_lds")
+        assert last_prefetch < body.find("global_store_dwordx4")

@@ -32,12 +32,22 @@ def test_adam_bytes_per_element():
     assert bench.adam_bytes_per_element("f32", "bf16") == 26   # 4+2+4+4 read, 4+4+4 written
 
 
-def test_traffic_record_tracks_its_source():
-    # the committed apply record names the current source's hash and a positive byte count
-    t = bench.measured_traffic("apply", "gpt2_124m")
-    assert t is not None and t > 0
-    # no record for a workload that has none
-    assert bench.measured_traffic("apply", "attn_768") is None
+def test_traffic_record_tracks_its_source(tmp_path, monkeypatch):
+    """A traffic record counts only while the source it names by hash is unchanged."""
+    import hashlib
+    csrc = tmp_path / "orthogonalized_momentum_optimizer_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    src = csrc / "ns_apply_bf16.hip"
+    src.write_text("// kernel source\n")
+    digest = hashlib.sha256(src.read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "apply_gpt2_124m_traffic.md").write_text(
+        f"traffic_bytes_per_launch: 1.5e8\nsource_sha256: {digest}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("apply", "gpt2_124m") == 1.5e8
+    assert bench.measured_traffic("apply", "attn_768") is None     # no record
+    src.write_text("// kernel source, changed\n")
+    assert bench.measured_traffic("apply", "gpt2_124m") is None    # stale record
 
 
 def test_more_than_one_gpu_is_refused():
@@ -45,3 +55,28 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in r.stderr or "--gpus 1" in r.stderr
+
+
+def test_cpu_baseline_times_the_oracle_only(monkeypatch):
+    """Input generation stays outside the timed region: with drawing made slow on purpose
+    (0.3 s per tensor) the reported rate still reflects the oracle's own time."""
+    import time as _time
+    wl = si.custom([(64, 256), (256, 64)], dtype="f32", steps=1, cfg_id=140, grad_std=1.0)
+    real_w, real_g = si.weight, si.grad
+
+    def slow_weight(*a):
+        _time.sleep(0.3)
+        return real_w(*a)
+
+    def slow_grad(*a):
+        _time.sleep(0.3)
+        return real_g(*a)
+
+    monkeypatch.setattr(bench.si, "weight", slow_weight)
+    monkeypatch.setattr(bench.si, "grad", slow_grad)
+    out = bench.cpu_baseline(wl, budget_s=5.0)
+    # two tiny matrices: a whole step takes milliseconds in the oracle, far below the 1.2 s
+    # of drawing
+    assert out["value"] > 5.0, out
+    assert "not timed" in out["sample"]
+    assert out["kind"] == "oracle" and out["cores"] >= 1

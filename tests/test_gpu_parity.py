@@ -73,13 +73,6 @@ def test_gpt2_tiny_fp32_workload(precision):
     assert rel(W0 - W3, 3 * 0.02 * O_ref) <= TOL[precision]
 
 
-@pytest.mark.parametrize("precision", ["bf16", "f32"])
-def test_attn_768_workload(precision):
-    _announce(f"attn_768 {precision}")
-    wl = si.WORKLOADS["attn_768"]
-    steps = wl.steps if precision == "bf16" else 3
-    gpu = run_gpu(wl, steps, precision)
-    compare(wl, gpu, steps, precision)
 
 
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
@@ -103,22 +96,8 @@ def test_iid_student_t_entries():
     compare(wl, gpu, 3, "bf16")
 
 
-def test_gpt2_124m_full_size_sampled():
-    """All 72 matrices of the 124M set in one batched step; a sample of matrices of every
-    shape is compared with the oracle (matrices are independent of each other)."""
-    wl = si.WORKLOADS["gpt2_124m"]
-    watch = si.sample_indices(wl)
-    _announce(f"gpt2_124m full size, watch {watch}")
-    gpu = run_gpu(wl, 3, "bf16", watch=watch)
-    compare(wl, gpu, 3, "bf16")
 
 
-def test_gpt2_124m_full_size_f32_debug_sampled():
-    wl = si.WORKLOADS["gpt2_124m"]
-    watch = [0, 4, 5]
-    _announce(f"gpt2_124m full size f32 debug, watch {watch}")
-    gpu = run_gpu(wl, 2, "f32", watch=watch)
-    compare(wl, gpu, 2, "f32")
 
 
 def test_gpt2_124m_share8_all_matrices():
@@ -158,20 +137,8 @@ def test_more_groups_than_one_launch_holds():
     compare(wl, gpu, 2, "bf16")
 
 
-def test_tall_stress_full_size_sampled():
-    wl = si.WORKLOADS["tall_stress"]
-    watch = si.sample_indices(wl)
-    _announce(f"tall_stress full size, watch {watch}")
-    gpu = run_gpu(wl, 2, "bf16", watch=watch)
-    compare(wl, gpu, 2, "bf16")
 
 
-def test_gpt2_1p5b_full_size_sampled():
-    wl = si.WORKLOADS["gpt2_1p5b"]
-    watch = [0, 4, 287]
-    _announce(f"gpt2_1p5b full size, watch {watch}")
-    gpu = run_gpu(wl, 1, "bf16", watch=watch, gpu_fill_others=True)
-    compare(wl, gpu, 1, "bf16")
 
 
 def test_batch_equals_alone_bitwise():
@@ -340,6 +307,25 @@ def test_coefficient_schedule_polishes_singular_values():
         sv = np.linalg.svd(f64(y), compute_uv=False)
         spreads.append(float(np.max(np.abs(sv - 1.0))))
     assert spreads[0] > 0.15 and spreads[1] < 0.5 * spreads[0], spreads
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [1e-22, 1e22])
+@pytest.mark.parametrize("eps", [1e-7, 0.0])
+def test_extreme_gradient_scales(precision, scale, eps):
+    """Gradients whose entries sit near 1e-25 or 1e19 (N(0, 1e-3) draws times the scale,
+    stored in bf16). Squares of the small ones underflow fp32 and sums of squares of the
+    large ones overflow it, so the norm is summed in double and X0 is rescaled by a power of
+    two before the first Gram product. With eps = 0 the normalisation is exact, with the
+    default eps the small set is dominated by eps (O = p^5 applied to U / eps)."""
+    _announce(f"gradient scale {scale:g}, eps {eps:g}, {precision}")
+    wl = si.custom([(200, 328), (328, 200), (256, 256)], dtype="bf16", steps=2, cfg_id=120)
+    grads = [[(si.grad(wl, i, t).float() * scale).to(torch.bfloat16) for t in range(2)]
+             for i in range(wl.n)]
+    for g in grads:
+        assert all(torch.isfinite(x.float()).all() and x.float().abs().max() > 0 for x in g)
+    gpu = run_gpu(wl, 2, precision, cfg=make_config(eps=eps), grads=grads)
+    compare(wl, gpu, 2, precision, grads=grads, oracle_kw=dict(eps=eps))
 
 
 def test_non_nesterov_and_other_hyperparameters():
