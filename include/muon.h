@@ -151,6 +151,25 @@ size_t muon_plan_workspace_size(const muon_plan *plan);
 int muon_step(muon_plan *plan, const muon_matrix *mats, int64_t n, const muon_config *cfg,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the static device scratch behind muon_step_noalloc (64 MiB: the GPT-2-124M
+ * matrix set's share of one GPU out of 8 needs 61.2 MiB in the bf16 rounds). */
+#define MUON_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* muon_step without a workspace argument, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation). The
+ * kernels' scratch is a static device array of MUON_STATIC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends; the call allocates nothing (its
+ * first call on a device looks up the array's address there, once). Same arguments, results
+ * and conventions as muon_step otherwise, with these limits:
+ *   - a plan whose muon_plan_workspace_size exceeds MUON_STATIC_SCRATCH_BYTES is rejected
+ *     with MUON_ERR_WORKSPACE before anything is enqueued (use muon_step with a workspace);
+ *   - nothing in the scratch has to start at zero (every step writes each scratch element it
+ *     reads), and its contents after a call are unspecified;
+ *   - every call on a device shares that device's scratch: calls that may overlap on one
+ *     device (different streams, or host threads without ordering) race. Order them. */
+int muon_step_noalloc(muon_plan *plan, const muon_matrix *mats, int64_t n,
+                      const muon_config *cfg, hipStream_t stream);
+
 /* The orthogonalisation alone (no momentum, no parameter update), for in[i] (rows x cols of
  * grad_dtype) into out[i] (rows x cols of param_dtype): out = NS(in / (||in||_F + eps)) with
  * cfg's ns_steps, a, b, c and eps; cfg's lr, beta and nesterov are ignored. This is the

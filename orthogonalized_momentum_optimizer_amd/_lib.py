@@ -33,8 +33,9 @@ EXPORTED = (
     "muon_config_default", "muon_plan_create", "muon_plan_workspace_size", "muon_step",
     "muon_newton_schulz", "muon_plan_destroy", "muon_plan_set_profiling",
     "muon_plan_read_profile", "muon_status_string", "muon_last_error",
-    "muon_adam_config_default", "muon_cautious_adam_step",
+    "muon_adam_config_default", "muon_cautious_adam_step", "muon_step_noalloc",
 )
+MUON_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class MuonError(RuntimeError):
@@ -122,6 +123,9 @@ def lib() -> ctypes.CDLL:
     L.muon_step.argtypes = [vp, ctypes.POINTER(muon_matrix), i64, ctypes.POINTER(muon_config),
                             vp, sz, vp]
     L.muon_step.restype = ctypes.c_int
+    L.muon_step_noalloc.argtypes = [vp, ctypes.POINTER(muon_matrix), i64,
+                                    ctypes.POINTER(muon_config), ctypes.c_void_p]
+    L.muon_step_noalloc.restype = ctypes.c_int
     L.muon_newton_schulz.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i64,
                                      ctypes.POINTER(muon_config), vp, sz, vp]
     L.muon_newton_schulz.restype = ctypes.c_int
@@ -193,6 +197,11 @@ def muon_step(plan: int, mats, n: int, cfg: muon_config, workspace: int, workspa
               stream: int) -> None:
     """``mats``: a ctypes array of muon_matrix (or None when n == 0)."""
     _check(lib().muon_step(plan, mats, n, ctypes.byref(cfg), workspace, workspace_bytes, stream))
+
+
+def muon_step_noalloc(plan: int, mats, n: int, cfg: muon_config, stream: int) -> None:
+    """muon_step with the library's static device scratch instead of a workspace."""
+    _check(lib().muon_step_noalloc(plan, mats, n, ctypes.byref(cfg), stream))
 
 
 def muon_newton_schulz(plan: int, inputs: Sequence[int], outputs: Sequence[int],

@@ -59,7 +59,9 @@ class MuonPlan:
 
     def __init__(self, shapes: Sequence[Sequence[int]], param_dtypes: Sequence[torch.dtype],
                  grad_dtypes: Sequence[torch.dtype], precision: str = "bf16",
-                 device: Optional[torch.device] = None):
+                 device: Optional[torch.device] = None, workspace: bool = True):
+        """``workspace=False``: no workspace is allocated; only ``step_noalloc`` (the
+        library's static device scratch) can then run the step."""
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.pdt = [dtype_code(d) for d in param_dtypes]
         self.gdt = [dtype_code(d) for d in grad_dtypes]
@@ -68,9 +70,11 @@ class MuonPlan:
                                          self.pdt, self.gdt, _PREC[precision])
         self.ws_bytes = L.muon_plan_workspace_size(self.handle)
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-        # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
-        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
-        assert self.workspace.data_ptr() % 256 == 0
+        self.workspace = None
+        if workspace:
+            # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+            self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+            assert self.workspace.data_ptr() % 256 == 0
         self._mats = None
         self._mats_key = None
 
@@ -133,8 +137,25 @@ class MuonPlan:
         if row_vars is not None and len(row_vars) != n:
             raise ValueError(f"expected {n} row_var buffers")
         mats = self._matrices(params, grads, moms, outs, row_vars) if n else None
+        if self.workspace is None:
+            raise RuntimeError("this plan has no workspace: use step_noalloc")
         L.muon_step(self.handle, mats, n, cfg, self.workspace.data_ptr(), self.ws_bytes,
                     _stream_handle(stream))
+
+    def step_noalloc(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                     moms: Sequence[torch.Tensor], cfg: L.muon_config,
+                     outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                     stream: Optional[torch.cuda.Stream] = None,
+                     row_vars: Optional[Sequence[torch.Tensor]] = None) -> None:
+        """``step`` through muon_step_noalloc: the kernels' scratch is the library's static
+        device array (at most MUON_STATIC_SCRATCH_BYTES of workspace), nothing is allocated."""
+        n = len(self.shapes)
+        if not (len(params) == len(grads) == len(moms) == n):
+            raise ValueError(f"expected {n} params, grads and momentum buffers")
+        if row_vars is not None and len(row_vars) != n:
+            raise ValueError(f"expected {n} row_var buffers")
+        mats = self._matrices(params, grads, moms, outs, row_vars) if n else None
+        L.muon_step_noalloc(self.handle, mats, n, cfg, _stream_handle(stream))
 
     def newton_schulz(self, inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor],
                       cfg: L.muon_config, stream: Optional[torch.cuda.Stream] = None) -> None:
@@ -147,6 +168,8 @@ class MuonPlan:
                 raise ValueError(f"matrix {i}: contiguous {self.shapes[i]} tensors expected")
             if dtype_code(x.dtype) != self.gdt[i] or dtype_code(y.dtype) != self.pdt[i]:
                 raise TypeError(f"matrix {i}: dtypes differ from the plan's")
+        if self.workspace is None:
+            raise RuntimeError("this plan has no workspace")
         L.muon_newton_schulz(self.handle, [x.data_ptr() for x in inputs],
                              [y.data_ptr() for y in outputs], cfg, self.workspace.data_ptr(),
                              self.ws_bytes, _stream_handle(stream))

@@ -59,6 +59,29 @@ int main(void) {
   cfg.row_equalize = 0;
   muon_plan_destroy(plan);
 
+  /* the static-scratch entry point: a plan larger than its scratch is rejected before any
+   * HIP call (24 matrices of 768 x 3072: 245 MiB of workspace), an empty plan is a no-op */
+  {
+    int64_t br[24], bc[24];
+    muon_dtype bd[24];
+    for (int i = 0; i < 24; ++i) {
+      br[i] = 768;
+      bc[i] = 3072;
+      bd[i] = MUON_DT_BF16;
+    }
+    muon_plan *big = NULL;
+    CHECK(muon_plan_create(&big, br, bc, bd, bd, 24, MUON_NS_BF16) == MUON_OK);
+    CHECK(muon_plan_workspace_size(big) > MUON_STATIC_SCRATCH_BYTES);
+    CHECK(muon_step_noalloc(big, NULL, 24, &cfg, 0) == MUON_ERR_WORKSPACE);
+    CHECK(strstr(muon_last_error(), "static scratch") != NULL);
+    muon_plan_destroy(big);
+    muon_plan *none = NULL;
+    CHECK(muon_plan_create(&none, NULL, NULL, NULL, NULL, 0, MUON_NS_BF16) == MUON_OK);
+    CHECK(muon_step_noalloc(none, NULL, 0, &cfg, 0) == MUON_OK);
+    CHECK(muon_step_noalloc(NULL, NULL, 0, &cfg, 0) == MUON_ERR_INVALID_ARG);
+    muon_plan_destroy(none);
+  }
+
   /* cautious Adam: defaults and validation */
   muon_adam_config acfg;
   muon_adam_config_default(&acfg);

@@ -419,3 +419,31 @@ def test_random_plans_workspace_model(mats, prec_esz):
         assert L.muon_plan_workspace_size(p) == _ws_expected(list(zip(rows, cols)), esz)
     finally:
         L.muon_plan_destroy(p)
+
+
+def test_noalloc_rejects_plans_beyond_the_static_scratch():
+    """muon_step_noalloc checks the plan's workspace against its static scratch before any
+    HIP call: the GPT-2-124M set (490 MiB) is refused with a message naming both sizes, the
+    8-GPU share (61.2 MiB) fits, an empty plan is a no-op."""
+    import seeded_inputs as si
+    full = si.WORKLOADS["gpt2_124m"].shapes
+    p = L.muon_plan_create([r for r, _ in full], [c for _, c in full], [0] * len(full),
+                           [0] * len(full))
+    try:
+        assert L.muon_plan_workspace_size(p) > L.MUON_STATIC_SCRATCH_BYTES
+        with pytest.raises(L.MuonError) as e:
+            L.muon_step_noalloc(p, None, len(full), L.muon_config_default(), 0)
+        assert e.value.status == L.MUON_ERR_WORKSPACE
+        assert str(L.MUON_STATIC_SCRATCH_BYTES) in str(e.value)
+    finally:
+        L.muon_plan_destroy(p)
+    share = si.WORKLOADS["gpt2_124m_share8"].shapes
+    p = L.muon_plan_create([r for r, _ in share], [c for _, c in share], [0] * len(share),
+                           [0] * len(share))
+    try:
+        assert 0 < L.muon_plan_workspace_size(p) <= L.MUON_STATIC_SCRATCH_BYTES
+    finally:
+        L.muon_plan_destroy(p)
+    p = L.muon_plan_create([], [], [], [])
+    L.muon_step_noalloc(p, None, 0, L.muon_config_default(), 0)
+    L.muon_plan_destroy(p)
