@@ -140,10 +140,13 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
         if (j < g.n && L >= g.g[j].first) k = j;
     }
     const ApplyGroup& q = kMulti ? kernel_args<ApplyArgs>()->g[k] : g.g[0];
+    // A matrix's tiles go column by column (the tiles_m row tiles sharing one column panel
+    // of X are consecutive), so the blocks an XCD runs at once share X's column panels and
+    // B' (all of B' is used by every column): a wide matrix's X is then fetched about once.
     const int l = L - q.first;
     c.bidx = l / q.per_mat;
     const int tt = l - c.bidx * q.per_mat;
-    const int I = tt / q.tiles_n, J = tt - (tt / q.tiles_n) * q.tiles_n;
+    const int J = tt / g.tiles_m, I = tt - J * g.tiles_m;
     const size_t mn = (size_t)g.mp * q.np;
     c.row0 = I * TM;
     c.col0 = J * TN;
