@@ -89,10 +89,22 @@ __device__ __forceinline__ const T* kernel_args() {
 }
 
 
+// vmcnt <= 16 + extra for a wave-uniform even `extra` below 2 kN (a chain of immediates: the
+// wait's count is an instruction field)
+template <int kN>
+__device__ __forceinline__ void vm_wait_16_plus(int extra) {
+  static_for<kN>([&](auto E) {
+    constexpr int e = 2 * decltype(E)::value;
+    if (extra == e) vm_wait<16 + e>();
+  });
+}
+
 // The kernel body. kMulti: the launch holds several groups (tile -> group lookup); a single
 // group's tiles skip the lookup and the dependent argument load it needs. kScaled: the first
 // round, whose output is scaled by s1 (every group of a launch has its scales, or none has).
-template <bool kMulti, bool kScaled>
+// kDefer: how many of a wave's 32 output stores per tile are held back and issued two per
+// iteration during the next tile's first iterations (0: all at the tile's end; see below).
+template <bool kMulti, bool kScaled, int kDefer>
 __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
   __shared__ u32x4 smem[NSTAGE * kUnitsStage];  // 128 KB ring
 
@@ -217,9 +229,14 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, f.av[i]);
   };
   f32x16 acc[4][4];
-  auto mfma = [&](int m, const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+  // FIRST: the tile's first K step, whose products start from a zero accumulator operand
+  // (used where the step is unrolled; elsewhere the accumulators are zeroed before the tile)
+  auto mfma = [&](int m, const bf16x8 (&af)[4], const bf16x8 (&bf)[4], auto first_t) {
     const int i = m >> 2, j = m & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    if constexpr (decltype(first_t)::value)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], f32x16{}, 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
   };
   // Waits for this wave's loads of a stage, then the block barrier: that stage is complete
   // for every wave. The vector-memory counter completes loads and stores in issue order, so
@@ -254,30 +271,73 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
   Frags f0, f1;
   Tile cur;
   int stores = 0;  // output stores of the previous tile issued after this tile's prefetch
-  auto iteration = [&](int kt, auto refill_t, auto more_t) {
+
+  // ---- deferred output (kDefer > 0) ----
+  // All blocks reach a tile's end at about the same time, so storing every output tile at
+  // its end sends the whole device's output out in one burst bound by HBM bandwidth (per-block
+  // timestamps: 8.4k cycles per tile for the stores alone at K = 768, against ~29.5k in the
+  // loop). With kDefer > 0 the tile's last kDefer chunks are kept in registers as bf16 and
+  // issued two per iteration during the next tile's first kDefer / 2 iterations (the block's
+  // last tile issues them after its loop). Chunk c (0..31) of a wave is accumulator block
+  // (c / 8, (c / 2) % 4), register quads 4 (c % 2) and 4 (c % 2) + 1 paired across the lane
+  // halves: 16 bytes per lane. A wave stores chunk c if its rows lie inside the matrix and,
+  // for (c / 2) % 4 >= 2, if the tile's right half does too (`mode`: 0 no chunk, 1 all, 2
+  // the left half only); the waits below count exactly the stores issued.
+  constexpr int kImm = 32 - kDefer;
+  constexpr int kHead = kDefer > 0 ? kDefer / 2 + 2 : 0;  // iterations whose waits count them
+  uint32_t outv[4 * kDefer + 4];
+  char* pseg = nullptr;  // the pending tile's lane address of chunk 0
+  int p_np = 0;
+  int mode = 0;
+  auto chunk_addr = [&](int c) {
+    return pseg + (size_t)64 * p_np * (c >> 3) + 2048 * ((c >> 1) & 3) + 16 * (2 * (c & 1));
+  };
+  auto chunk_stored = [&](int c) { return mode == 1 || (mode == 2 && ((c >> 1) & 3) < 2); };
+  // deferred stores issued in iteration k of a tile (both of its chunks share (c / 2) % 4)
+  auto deferred_in = [&](int k) {
+    return (k >= 0 && k < kDefer / 2 && chunk_stored(kImm + 2 * k)) ? 2 : 0;
+  };
+
+  // One K step. DD: the first of this iteration's two deferred chunks (-1: none); extra:
+  // stores issued after the loads of stage kt + 1, when kDefer > 0.
+  using NoD = std::integral_constant<int, -1>;
+  auto iteration = [&](int kt, auto refill_t, auto more_t, auto dd_t, int extra, auto first_t) {
     constexpr bool refill = decltype(refill_t)::value, more = decltype(more_t)::value;
+    constexpr int dd = decltype(dd_t)::value;
     const uint32_t cb = stage_base(kt);
     const uint32_t va1 = cb + aoff1, vb = cb + boff;
     __builtin_amdgcn_sched_barrier(0);
     static_for<16>([&](auto M) {
       constexpr int m = decltype(M)::value;
-      mfma(m, a0, b0);
+      mfma(m, a0, b0, first_t);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (m < 12) lds_op<1, m>(va1, vb, f1);
+      if constexpr (dd >= 0 && (m == 12 || m == 14)) {
+        constexpr int d = dd + (m == 14 ? 1 : 0);
+        if (chunk_stored(kImm + d))
+          *reinterpret_cast<u32x4*>(chunk_addr(kImm + d)) =
+              u32x4{outv[4 * d], outv[4 * d + 1], outv[4 * d + 2], outv[4 * d + 3]};
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     ready(f1, a1, b1);  // slice 1 is in registers: this wave is done reading stage kt
     if constexpr (more) {
-      const int st = kt + 1 < NSTAGE ? stores : 0;  // stage kt + 1 was prefetched
-      if constexpr (refill) stage_ready(NSTAGE - 2, st);
-      else stage_ready(min(NSTAGE - 2, KT - 2 - kt), st);
+      if constexpr (kDefer > 0 && refill) {
+        vm_wait_16_plus<(kImm + 6) / 2 + 1>(extra);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        const int st = kt + 1 < NSTAGE ? stores : 0;  // stage kt + 1 was prefetched
+        if constexpr (refill) stage_ready(NSTAGE - 2, st);
+        else stage_ready(min(NSTAGE - 2, KT - 2 - kt), st);
+      }
     }
     const uint32_t nxt = stage_base(kt + 1);
     const uint32_t va0n = nxt + aoff0, vbn = nxt + boff;
     __builtin_amdgcn_sched_barrier(0);
     static_for<16>([&](auto M) {
       constexpr int m = decltype(M)::value;
-      mfma(m, a1, b1);
+      mfma(m, a1, b1, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (refill && m < 8) dma_op(cur, kt + NSTAGE, m);
       if constexpr (more && m >= 2 && m < 14) lds_op<0, m - 2>(va0n, vbn, f0);
@@ -296,20 +356,45 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
       for (int op = 0; op < 8; ++op) dma_op(cur, st, op);  // KT >= 4: mp is a multiple of 128
   }
   for (; L < hi; L += nb) {
+    if constexpr (kDefer == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    stage_ready(NSTAGE - 1, stores);
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    if constexpr (kDefer > 0) {  // stage 0: three stages of loads and the immediate stores later
+      static_for<kImm + 1>([&](auto E) {
+        if (stores == decltype(E)::value) vm_wait<3 * kLoadsPerStage + decltype(E)::value>();
+      });
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      stage_ready(NSTAGE - 1, stores);
+    }
     static_for<12>([&](auto OP) { lds_op<0, decltype(OP)::value>(lds0 + aoff0, lds0 + boff, f0); });
     ready(f0, a0, b0);
 
     int kt = 0;
-    for (; kt < KT - NSTAGE; ++kt) iteration(kt, std::true_type{}, std::true_type{});
-    for (; kt < KT - 1; ++kt) iteration(kt, std::false_type{}, std::true_type{});
-    iteration(KT - 1, std::false_type{}, std::false_type{});
+    if constexpr (kDefer > 0) {
+      // The wait for stage k + 1 leaves pending the two later stages' loads (16) and the
+      // stores issued after that stage's loads: the previous tile's immediate stores when the
+      // stage was prefetched (k + 1 < 4) and the deferred stores of iterations k - 2 .. k.
+      static_for<kHead>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        const int extra = (k + 1 < NSTAGE ? stores : 0) + deferred_in(k - 2) +
+                          deferred_in(k - 1) + deferred_in(k);
+        iteration(k, std::true_type{}, std::true_type{},
+                  std::integral_constant<int, (k < kDefer / 2) ? 2 * k : -1>{}, extra,
+                  std::integral_constant<bool, k == 0>{});
+      });
+      kt = kHead;
+    }
+    using F = std::false_type;
+    for (; kt < KT - NSTAGE; ++kt) iteration(kt, std::true_type{}, std::true_type{}, NoD{}, 0, F{});
+    for (; kt < KT - 1; ++kt) iteration(kt, std::false_type{}, std::true_type{}, NoD{}, 0, F{});
+    iteration(KT - 1, std::false_type{}, std::false_type{}, NoD{}, 0, F{});
 
     // every wave is done with the ring: the next tile's first stages load while this tile's
     // output is stored
@@ -340,10 +425,48 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
     // padded matrix or wholly outside.
     const int half = lane >> 5;
     const bool rows_in = row0 + wr * 128 < g.mp, right_in = col0 + 128 < np;
-    stores = rows_in ? (right_in ? 32 : 16) : 0;  // the stores issued below
     char* const seg0 = reinterpret_cast<char*>(
         out + toff(min(row0 + wr * 128 + (lane & 31), g.mp - 1), col0 + 32 * wc + 8 * half, np));
-    {
+    if constexpr (kDefer > 0) {
+      // the chunks in order c = 8i + 2j + q/2: the first kImm stored now, the rest kept
+      mode = __builtin_amdgcn_readfirstlane(rows_in ? (right_in ? 1 : 2) : 0);
+      pseg = seg0;
+      p_np = np;
+      stores = 0;
+      static_for<32>([&](auto C) {
+        constexpr int ch = decltype(C)::value;
+        constexpr int i = ch >> 3, j = (ch >> 1) & 3, q = 2 * (ch & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xv = acc[i][j][4 * q + e];
+          v[e] = kScaled ? xv * s : xv;
+        }
+        uint32_t lo[2] = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        uint32_t hi[2] = {pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+          lo[d] = r[0];
+          hi[d] = r[1];
+        }
+        if constexpr (ch < kImm) {
+          if (chunk_stored(ch)) {
+            *reinterpret_cast<u32x4*>(chunk_addr(ch)) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            stores += 1;
+          }
+        } else {
+          constexpr int d = ch - kImm;
+          outv[4 * d] = lo[0];
+          outv[4 * d + 1] = lo[1];
+          outv[4 * d + 2] = hi[0];
+          outv[4 * d + 3] = hi[1];
+        }
+      });
+      stores = __builtin_amdgcn_readfirstlane(stores);
+    } else {
+      stores = rows_in ? (right_in ? 32 : 16) : 0;  // the stores issued below
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -372,20 +495,57 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
         }
     }
   }
+  if constexpr (kDefer > 0) {  // the block's last tile: its kept chunks
+    static_for<kDefer>([&](auto D) {
+      constexpr int d = decltype(D)::value;
+      if (chunk_stored(kImm + d))
+        *reinterpret_cast<u32x4*>(chunk_addr(kImm + d)) =
+            u32x4{outv[4 * d], outv[4 * d + 1], outv[4 * d + 2], outv[4 * d + 3]};
+    });
+  }
 }
 
-__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) { apply_tiles<false, false>(g); }
+// Stores per wave held back to the next tile (24 of 32: the registers for 32 would spill), for
+// launches of K >= 24 stages (mp >= 768: the held stores go out during the next tile's first
+// 12 iterations) whose operands and output together fit the 256 MB Infinity Cache. When they
+// do not (e.g. 96 matrices of 768 x 3072, 1 GB), the loads of the loop come from HBM and the
+// held stores inside the loop slowed it more than the end-of-tile burst cost (per-block
+// timestamps: ~38k against ~32k cycles per 24-step loop), so those launches store at the
+// tile's end.
+constexpr int kDeferStores = 24;
+constexpr int kDeferMinKt = 24;
+constexpr size_t kDeferMaxBytes = size_t(256) << 20;
+
+__global__ __launch_bounds__(256) void ns_apply_bf16(ApplyArgs g) {
+  apply_tiles<false, false, 0>(g);
+}
 
 __global__ __launch_bounds__(256) void ns_apply_bf16_scaled(ApplyArgs g) {
-  apply_tiles<false, true>(g);
+  apply_tiles<false, true, 0>(g);
 }
 
 __global__ __launch_bounds__(256) void ns_apply_bf16_groups(ApplyArgs g) {
-  apply_tiles<true, false>(g);
+  apply_tiles<true, false, 0>(g);
 }
 
 __global__ __launch_bounds__(256) void ns_apply_bf16_groups_scaled(ApplyArgs g) {
-  apply_tiles<true, true>(g);
+  apply_tiles<true, true, 0>(g);
+}
+
+__global__ __launch_bounds__(256) void ns_apply_defer_bf16(ApplyArgs g) {
+  apply_tiles<false, false, kDeferStores>(g);
+}
+
+__global__ __launch_bounds__(256) void ns_apply_defer_bf16_scaled(ApplyArgs g) {
+  apply_tiles<false, true, kDeferStores>(g);
+}
+
+__global__ __launch_bounds__(256) void ns_apply_defer_bf16_groups(ApplyArgs g) {
+  apply_tiles<true, false, kDeferStores>(g);
+}
+
+__global__ __launch_bounds__(256) void ns_apply_defer_bf16_groups_scaled(ApplyArgs g) {
+  apply_tiles<true, true, kDeferStores>(g);
 }
 
 // ---- 128x128 tiles, for sets whose 256x256 tiles would leave most compute units idle ----
@@ -566,6 +726,19 @@ __global__ __launch_bounds__(256) void ns_apply128_bf16(ApplyArgs g) {
 
 // launches the grid for a single group or for several, first round (scaled) or not
 void launch_apply_grid(const ApplyArgs& a, bool scaled, dim3 grid, hipStream_t s) {
+  size_t bytes = 0;  // B', X and X' of every matrix of the launch
+  for (int k = 0; k < a.n; ++k) {
+    const int end = k + 1 < a.n ? a.g[k + 1].first : a.total_tiles;
+    const size_t batch = (size_t)(end - a.g[k].first) / a.g[k].per_mat;
+    bytes += batch * 2 * ((size_t)a.mp * a.mp + 2 * (size_t)a.mp * a.g[k].np);
+  }
+  if (a.mp / TK >= kDeferMinKt && bytes <= kDeferMaxBytes) {
+    if (a.n > 1 && scaled) launch_k(ns_apply_defer_bf16_groups_scaled, grid, dim3(256), 0, s, a);
+    else if (a.n > 1) launch_k(ns_apply_defer_bf16_groups, grid, dim3(256), 0, s, a);
+    else if (scaled) launch_k(ns_apply_defer_bf16_scaled, grid, dim3(256), 0, s, a);
+    else launch_k(ns_apply_defer_bf16, grid, dim3(256), 0, s, a);
+    return;
+  }
   if (a.n > 1 && scaled) launch_k(ns_apply_bf16_groups_scaled, grid, dim3(256), 0, s, a);
   else if (a.n > 1) launch_k(ns_apply_bf16_groups, grid, dim3(256), 0, s, a);
   else if (scaled) launch_k(ns_apply_bf16_scaled, grid, dim3(256), 0, s, a);

@@ -214,3 +214,25 @@ def test_apply_tile_start_waits_count_the_previous_stores():
         body = "\n".join(ln.strip() for ln in f.splitlines())
         last_prefetch = body.rfind("global_load_lds")
         assert last_prefetch < body.find("global_store_dwordx4")
+
+
+def test_apply_kernels_use_no_scratch_and_defer_their_stores():
+    """Every apply kernel keeps its values in registers (no scratch: a spill would add vector-
+    memory operations that the counted waits do not expect). The kernels that hold stores back
+    issue 8 at a tile's end, 2 in each of the next tile's first 12 iterations and the held 24
+    after the block's last tile: 56 store instructions, each behind its own condition."""
+    import re
+    try:
+        path = build.device_asm("ns_apply_bf16.hip")
+    except RuntimeError as e:
+        pytest.skip(str(e))
+    text = open(path).read()
+    meta = dict(zip(re.findall(r"\.name:\s+(_Z\S+)", text),
+                    re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)))
+    assert meta and all(v == "0" for v in meta.values()), meta
+    funcs = re.split(r"\n(?=_Z\S+: ; @)", text)
+    defer = [f for f in funcs if re.match(r"_ZN4muon12_GLOBAL__N_1\d+ns_apply_defer_bf16", f)]
+    assert len(defer) == 4
+    for f in defer:
+        assert len(re.findall(r"\n\s*global_store_dwordx4", f)) == 8 + 12 * 2 + 24
+        assert "v_accvgpr_write" not in f     # the first K step starts from a zero operand
