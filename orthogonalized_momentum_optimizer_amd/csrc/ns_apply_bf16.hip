@@ -511,7 +511,8 @@ __device__ __forceinline__ void apply_tiles(const ApplyArgs& g) {
 // do not (e.g. 96 matrices of 768 x 3072, 1 GB), the loads of the loop come from HBM and the
 // held stores inside the loop slowed it more than the end-of-tile burst cost (per-block
 // timestamps: ~38k against ~32k cycles per 24-step loop), so those launches store at the
-// tile's end.
+// tile's end, and so does the first round (whose X0 comes from the momentum kernel: holding
+// its stores measured 76.4 against 74.6 us per launch on the GPT-2-124M set).
 constexpr int kDeferStores = 24;
 constexpr int kDeferMinKt = 24;
 constexpr size_t kDeferMaxBytes = size_t(256) << 20;
@@ -536,17 +537,11 @@ __global__ __launch_bounds__(256) void ns_apply_defer_bf16(ApplyArgs g) {
   apply_tiles<false, false, kDeferStores>(g);
 }
 
-__global__ __launch_bounds__(256) void ns_apply_defer_bf16_scaled(ApplyArgs g) {
-  apply_tiles<false, true, kDeferStores>(g);
-}
-
 __global__ __launch_bounds__(256) void ns_apply_defer_bf16_groups(ApplyArgs g) {
   apply_tiles<true, false, kDeferStores>(g);
 }
 
-__global__ __launch_bounds__(256) void ns_apply_defer_bf16_groups_scaled(ApplyArgs g) {
-  apply_tiles<true, true, kDeferStores>(g);
-}
+
 
 // ---- 128x128 tiles, for sets whose 256x256 tiles would leave most compute units idle ----
 // The same product on 128x128 output tiles, one tile per block (no persistent loop): 256
@@ -732,10 +727,8 @@ void launch_apply_grid(const ApplyArgs& a, bool scaled, dim3 grid, hipStream_t s
     const size_t batch = (size_t)(end - a.g[k].first) / a.g[k].per_mat;
     bytes += batch * 2 * ((size_t)a.mp * a.mp + 2 * (size_t)a.mp * a.g[k].np);
   }
-  if (a.mp / TK >= kDeferMinKt && bytes <= kDeferMaxBytes) {
-    if (a.n > 1 && scaled) launch_k(ns_apply_defer_bf16_groups_scaled, grid, dim3(256), 0, s, a);
-    else if (a.n > 1) launch_k(ns_apply_defer_bf16_groups, grid, dim3(256), 0, s, a);
-    else if (scaled) launch_k(ns_apply_defer_bf16_scaled, grid, dim3(256), 0, s, a);
+  if (!scaled && a.mp / TK >= kDeferMinKt && bytes <= kDeferMaxBytes) {
+    if (a.n > 1) launch_k(ns_apply_defer_bf16_groups, grid, dim3(256), 0, s, a);
     else launch_k(ns_apply_defer_bf16, grid, dim3(256), 0, s, a);
     return;
   }
