@@ -181,6 +181,27 @@ int muon_newton_schulz(muon_plan *plan, const void *const *in, void *const *out,
 
 void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
 
+/* Upper bound of muon_plan_set_concurrency's stream count. */
+#define MUON_MAX_STREAMS 4
+
+/* Lets later calls of muon_step, muon_step_noalloc and muon_newton_schulz on this plan run
+ * its shape groups concurrently: the first group stays on the call's stream, the others run
+ * on up to streams - 1 streams of the plan's own (created here, at the default priority, on
+ * the current device, with the events that fork them from and join them back to the call's
+ * stream; muon_plan_destroy releases them). Groups share no buffer, and each group's
+ * kernels and their order are unchanged, so results are bitwise those of the sequential
+ * step; a concurrent step fills the device with one group's kernels while another group's
+ * drain. streams = 1 (the default of a new plan) releases the streams and runs the groups
+ * in sequence. Calls run in sequence all the same on another device than the one this was
+ * called on, while profiling is enabled (each kernel is then timed alone), and for sets
+ * larger than 16 apply tiles of 256x256 per compute unit in all, whose long kernels measured
+ * faster in sequence. Plans whose groups share launches (sets too small to fill the device
+ * group by group) are unaffected.
+ * Returns MUON_ERR_INVALID_ARG for streams outside [1, MUON_MAX_STREAMS] and MUON_ERR_HIP if
+ * the HIP runtime cannot create the streams (the plan is then left sequential). Call it
+ * outside stream capture; steps on the plan may be captured afterwards. */
+int muon_plan_set_concurrency(muon_plan *plan, int streams);
+
 /* Kernel timing for measurement. When enabled, every later muon_step/muon_newton_schulz
  * times each kernel launch with a HIP event pair that the launch itself updates with the
  * kernel's start and end (hipExtLaunchKernel; no marker packets are added to the stream).

@@ -34,7 +34,9 @@ EXPORTED = (
     "muon_newton_schulz", "muon_plan_destroy", "muon_plan_set_profiling",
     "muon_plan_read_profile", "muon_status_string", "muon_last_error",
     "muon_adam_config_default", "muon_cautious_adam_step", "muon_step_noalloc",
+    "muon_plan_set_concurrency",
 )
+MUON_MAX_STREAMS = 4
 MUON_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -133,6 +135,8 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_destroy.restype = None
     L.muon_plan_set_profiling.argtypes = [vp, ctypes.c_int]
     L.muon_plan_set_profiling.restype = ctypes.c_int
+    L.muon_plan_set_concurrency.argtypes = [vp, ctypes.c_int]
+    L.muon_plan_set_concurrency.restype = ctypes.c_int
     L.muon_plan_read_profile.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(i64), ctypes.c_int]
     L.muon_plan_read_profile.restype = ctypes.c_int
@@ -216,6 +220,10 @@ def muon_newton_schulz(plan: int, inputs: Sequence[int], outputs: Sequence[int],
 
 def muon_plan_set_profiling(plan: int, enable: bool) -> None:
     _check(lib().muon_plan_set_profiling(plan, 1 if enable else 0))
+
+
+def muon_plan_set_concurrency(plan: int, streams: int) -> None:
+    _check(lib().muon_plan_set_concurrency(plan, int(streams)))
 
 
 def muon_plan_read_profile(plan: int) -> dict:

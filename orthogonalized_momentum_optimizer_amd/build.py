@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
 SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip",
-           "ns_apply_bf16.hip", "ns_gemm_f32.hip", "cautious_adam.hip", "noalloc.hip"]
+           "ns_quad_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip", "cautious_adam.hip",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

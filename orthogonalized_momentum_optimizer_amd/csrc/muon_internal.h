@@ -110,6 +110,12 @@ hipError_t launch_poly_bf16(const NsGroup* groups, int n, float a, float b, floa
 hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s);  // X' = s1 B' X
 int device_cus();  // compute units of the current device
 hipError_t launch_gram256_bf16(const NsGroup* groups, int n, hipStream_t s);
+// Four 128x128 blocks per work item (ns_quad_bf16.hip), for groups with mp a multiple of
+// 256; mode 0 = gram, 1 = poly. quad_items: the group's work items.
+bool use_quad(const NsGroup& g);
+int quad_items(const NsGroup& g);
+hipError_t launch_quad_bf16(const NsGroup* const* groups, int n, int mode, float a, float b,
+                            float c, hipStream_t s);
 hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, float c,
                                hipStream_t s);
 // fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip): B = bA + cAA and

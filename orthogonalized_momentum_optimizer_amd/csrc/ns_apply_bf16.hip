@@ -762,11 +762,19 @@ hipError_t launch_apply_bf16(const NsGroup* groups, int n, hipStream_t s) {
   std::vector<bool> done(n, false);
   for (int k0 = 0; k0 < n; ++k0) {
     if (done[k0]) continue;
+    // a group that fills the device on its own gets a launch of its own; smaller groups
+    // share one (every XCD's L2 then serves fewer matrices at a time)
+    auto own_tiles = [&](int k) {
+      return ((groups[k].mp + TM - 1) / TM) * ((groups[k].np + TN - 1) / TN) * groups[k].batch;
+    };
     std::vector<const NsGroup*> set;
     for (int k = k0; k < n && (int)set.size() < kMaxLaunchGroups; ++k)
       if (!done[k] && groups[k].mp == groups[k0].mp) {
+        const bool alone = own_tiles(k) >= cus;
+        if (alone && !set.empty()) continue;
         done[k] = true;
         set.push_back(&groups[k]);
+        if (alone) break;
       }
     auto fill = [&](int tm, int tn) {
       ApplyArgs a{};

@@ -99,6 +99,12 @@ struct muon_plan {
   int ev_used = 0;             // pairs recorded by the pending call
   double prof_ms[MUON_KERNEL_KINDS] = {};
   int64_t prof_launches[MUON_KERNEL_KINDS] = {};
+  // concurrent shape groups (muon_plan_set_concurrency): side streams at the default
+  // priority and their fork/join events, made on device `dev`
+  int dev = -1;
+  std::vector<hipStream_t> side;
+  hipEvent_t fork = nullptr;
+  std::vector<hipEvent_t> join;
 };
 
 namespace {
@@ -200,6 +206,41 @@ bool merge_groups(const muon_plan* p) {
   return tiles < (long long)kMergeTilesPerCu * device_cus();
 }
 
+// Whether a step that may run its groups concurrently does: when their kernels are short
+// enough that each launch's ramp, tail and write-out leave the device partly idle, which the
+// other groups' kernels then fill. At most kConcurrentTilesPerCu apply tiles of 256x256 per
+// compute unit in all: the GPT-2-124M set (5.1 per unit) measured 2-3% faster per step
+// with its two groups side by side, the GPT-2-1.5B set (102 per unit), whose kernels run for
+// milliseconds, 0.9% slower.
+constexpr int kConcurrentTilesPerCu = 16;
+
+bool concurrent_groups(const muon_plan* p) {
+  long long tiles = 0;
+  for (const Group& G : p->groups)
+    tiles += (long long)((G.mp + 255) / 256) * ((G.np + 255) / 256) * G.count;
+  return tiles <= (long long)kConcurrentTilesPerCu * device_cus();
+}
+
+// Side streams of a step that runs its shape groups concurrently (muon_plan_set_concurrency):
+// none while profiling (each kernel is then timed alone), on another device than the one
+// they were made on, or for sets whose groups run faster in sequence (concurrent_groups).
+int side_streams(const muon_plan* p) {
+  if (p->side.empty() || p->prof || !concurrent_groups(p)) return 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != p->dev) return 0;
+  return (int)p->side.size();
+}
+
+void release_streams(muon_plan* p) {
+  for (hipStream_t st : p->side) (void)hipStreamDestroy(st);
+  for (hipEvent_t e : p->join) (void)hipEventDestroy(e);
+  if (p->fork) (void)hipEventDestroy(p->fork);
+  p->side.clear();
+  p->join.clear();
+  p->fork = nullptr;
+  p->dev = -1;
+}
+
 // The step: momentum, norm, the Newton-Schulz rounds and the update of each shape group,
 // either one group after the other or, for small sets (merge_groups), phase by phase over all
 // groups.
@@ -218,7 +259,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
   auto scales_of = [&](const Group& G) { return reinterpret_cast<float*>(base + G.off_scales); };
 
   // phase 1: momentum, norm partials, X0; then the norms
-  auto momentum_and_norm = [&](const Group& G) {
+  auto momentum_and_norm = [&](const Group& G, hipStream_t stream) {
     double* part = reinterpret_cast<double*>(base + G.off_part);
     for (int si : G.sets) {
       const LaunchSet& S = p->sets[si];
@@ -253,7 +294,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
 
   // phase 2: Newton-Schulz rounds over the listed groups, ping-pong between x0 and x1; the
   // bf16 products take all of them in one launch each. Returns where each group's result is.
-  auto rounds = [&](const std::vector<int>& gis) {
+  auto rounds = [&](const std::vector<int>& gis, hipStream_t stream) {
     std::vector<NsGroup> N(gis.size());
     for (size_t k = 0; k < gis.size(); ++k) {
       const Group& G = p->groups[gis[k]];
@@ -292,7 +333,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
   };
 
   // phase 3: row equaliser (optional), parameter update (and O output) from X = xres
-  auto finish = [&](const Group& G, char* xres) {
+  auto finish = [&](const Group& G, char* xres, hipStream_t stream) {
     float* scales = scales_of(G);
     float* rowsum = reinterpret_cast<float*>(base + G.off_rowsum);
     float* rowf = reinterpret_cast<float*>(base + G.off_rowf);
@@ -356,14 +397,29 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
     std::vector<int> all(ng);
     for (int gi = 0; gi < ng; ++gi) {
       all[gi] = gi;
-      momentum_and_norm(p->groups[gi]);
+      momentum_and_norm(p->groups[gi], stream);
     }
-    const std::vector<char*> res = rounds(all);
-    for (int gi = 0; gi < ng; ++gi) finish(p->groups[gi], res[gi]);
+    const std::vector<char*> res = rounds(all, stream);
+    for (int gi = 0; gi < ng; ++gi) finish(p->groups[gi], res[gi], stream);
   } else {
+    const int nside = side_streams(p);
+    if (nside > 0) {
+      if (hipError_t e = hipEventRecord(p->fork, stream))
+        return fail(MUON_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+      for (int k = 0; k < nside; ++k)
+        if (hipError_t e = hipStreamWaitEvent(p->side[k], p->fork, 0))
+          return fail(MUON_ERR_HIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
+    }
     for (int gi = 0; gi < ng && L.status == MUON_OK; ++gi) {
-      momentum_and_norm(p->groups[gi]);
-      finish(p->groups[gi], rounds({gi})[0]);
+      const hipStream_t st = (gi == 0 || nside == 0) ? stream : p->side[(gi - 1) % nside];
+      momentum_and_norm(p->groups[gi], st);
+      finish(p->groups[gi], rounds({gi}, st)[0], st);
+    }
+    for (int k = 0; k < nside; ++k) {
+      if (hipError_t e = hipEventRecord(p->join[k], p->side[k]))
+        return fail(MUON_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+      if (hipError_t e = hipStreamWaitEvent(stream, p->join[k], 0))
+        return fail(MUON_ERR_HIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
     }
   }
   return L.status;
@@ -594,7 +650,40 @@ void muon_plan_destroy(muon_plan* plan) {
     prof_collect(plan);
     for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
   }
+  release_streams(plan);
   delete plan;
+}
+
+int muon_plan_set_concurrency(muon_plan* plan, int streams) {
+  clear_error();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (streams < 1 || streams > MUON_MAX_STREAMS)
+    return fail(MUON_ERR_INVALID_ARG, "streams = %d outside [1, %d]", streams, MUON_MAX_STREAMS);
+  release_streams(plan);
+  const int want = std::min<int>(streams, (int)plan->groups.size()) - 1;
+  if (want <= 0) return MUON_OK;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->fork, hipEventDisableTiming);
+  for (int k = 0; k < want && e == hipSuccess; ++k) {
+    hipStream_t st = nullptr;
+    hipEvent_t ev = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) break;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipStreamDestroy(st);
+      break;
+    }
+    plan->side.push_back(st);
+    plan->join.push_back(ev);
+  }
+  if (e != hipSuccess) {
+    release_streams(plan);
+    return fail(MUON_ERR_HIP, "creating the plan's streams failed: %s", hipGetErrorString(e));
+  }
+  plan->dev = dev;
+  return MUON_OK;
 }
 
 int muon_plan_set_profiling(muon_plan* plan, int enable) {

@@ -59,9 +59,11 @@ class MuonPlan:
 
     def __init__(self, shapes: Sequence[Sequence[int]], param_dtypes: Sequence[torch.dtype],
                  grad_dtypes: Sequence[torch.dtype], precision: str = "bf16",
-                 device: Optional[torch.device] = None, workspace: bool = True):
+                 device: Optional[torch.device] = None, workspace: bool = True,
+                 streams: int = L.MUON_MAX_STREAMS):
         """``workspace=False``: no workspace is allocated; only ``step_noalloc`` (the
-        library's static device scratch) can then run the step."""
+        library's static device scratch) can then run the step. ``streams``: shape groups a
+        step may run concurrently (muon_plan_set_concurrency; 1 runs them in sequence)."""
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.pdt = [dtype_code(d) for d in param_dtypes]
         self.gdt = [dtype_code(d) for d in grad_dtypes]
@@ -77,6 +79,11 @@ class MuonPlan:
             assert self.workspace.data_ptr() % 256 == 0
         self._mats = None
         self._mats_key = None
+        with torch.cuda.device(dev):
+            L.muon_plan_set_concurrency(self.handle, streams)
+
+    def set_concurrency(self, streams: int):
+        L.muon_plan_set_concurrency(self.handle, streams)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -57,6 +57,11 @@ int main(void) {
   cfg.row_equalize = 1;
   CHECK(muon_step(plan, mats, 3, &cfg, wsp, ws, 0) == MUON_ERR_INVALID_ARG);
   cfg.row_equalize = 0;
+  /* concurrency: the stream count is checked before any HIP call; 1 is sequential */
+  CHECK(muon_plan_set_concurrency(plan, 0) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_plan_set_concurrency(plan, MUON_MAX_STREAMS + 1) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_plan_set_concurrency(plan, 1) == MUON_OK);
+  CHECK(muon_plan_set_concurrency(NULL, 2) == MUON_ERR_INVALID_ARG);
   muon_plan_destroy(plan);
 
   /* the static-scratch entry point: a plan larger than its scratch is rejected before any

@@ -118,6 +118,18 @@ def test_plan_create_rejects_bad_precision():
     assert e.value.status == L.MUON_ERR_INVALID_ARG
 
 
+def test_set_concurrency_validates_its_arguments():
+    p = L.muon_plan_create([8, 300], [8, 600], [0, 0], [0, 0])   # two shape groups
+    for bad in (0, -1, L.MUON_MAX_STREAMS + 1):
+        with pytest.raises(L.MuonError) as e:
+            L.muon_plan_set_concurrency(p, bad)
+        assert e.value.status == L.MUON_ERR_INVALID_ARG
+        assert "streams" in L.muon_last_error()
+    L.muon_plan_set_concurrency(p, 1)   # sequential: makes no HIP call
+    L.muon_plan_destroy(p)
+    assert L.lib().muon_plan_set_concurrency(None, 2) == L.MUON_ERR_INVALID_ARG
+
+
 def test_profile_calls_on_plan():
     p = L.muon_plan_create([8], [8], [0], [0])
     prof = L.muon_plan_read_profile(p)

@@ -75,8 +75,9 @@ def test_cpu_baseline_times_the_oracle_only(monkeypatch):
     monkeypatch.setattr(bench.si, "weight", slow_weight)
     monkeypatch.setattr(bench.si, "grad", slow_grad)
     out = bench.cpu_baseline(wl, budget_s=5.0)
-    # two tiny matrices: a whole step takes milliseconds in the oracle, far below the 1.2 s
-    # of drawing
-    assert out["value"] > 5.0, out
+    # two tiny matrices: a whole step takes milliseconds in the oracle; timing the 1.2 s of
+    # drawing per step would report below 0.84 steps/s (the bound leaves room for a loaded
+    # host)
+    assert out["value"] > 2.0, out
     assert "not timed" in out["sample"]
     assert out["kind"] == "oracle" and out["cores"] >= 1
