@@ -19,6 +19,11 @@ two staged gradient batches used alternately). Prints one JSON line:
              one launch per step, HBM bytes of the algorithm over the launch time; and the
              same Muon step with the per-row energy equaliser switched on (its extra cost)
 
+  mfma_bound the Newton-Schulz products' matrix-core issue bound: each product launch of a
+             round replayed with the same grid and MFMAs per wave but no memory traffic
+             (libmuon_mfma_loop.so), its time and shader clock; against it, the fraction of
+             that bound the products reach
+
   library_ceiling  what the vendor GEMM library (hipBLASLt, through torch.bmm / torch.matmul)
              reaches on the same box in the same run: the apply products of the workload's
              shape groups as plain batched GEMMs, and one large 8192^3 GEMM; a comparison
@@ -63,6 +68,101 @@ def kind_work(wl, ns_steps=5):
         w["momentum"] += r * c * (esz + 8.0)
         w["update"] += r * c * (2.0 * esz)
     return w
+
+
+def shape_groups(wl):
+    """The plan's shape groups: (count, mp, np) of the padded wide shapes (rows and cols
+    swapped when rows > cols, each rounded up to a multiple of 128)."""
+    from collections import Counter
+    cnt = Counter()
+    for r, c in wl.shapes:
+        m, n = min(r, c), max(r, c)
+        cnt[(-(-m // 128) * 128, -(-n // 128) * 128)] += 1
+    return [(b, mp, np_) for (mp, np_), b in sorted(cnt.items())]
+
+
+def product_launches(wl, cus):
+    """Grid, register tile and K steps of every bf16 product launch of one Newton-Schulz
+    round, group by group, as the library launches them (sets whose groups share launches
+    are not modelled: returns None). Each entry: (kind, group, blocks, nacc, iters, lds):
+    blocks of 256 threads, nacc 32x32 accumulator blocks per wave (16: a 128x128 register
+    tile, 4: 64x64), iters 32-deep K steps per wave of the busiest block, lds bytes per
+    block (which sets the blocks per compute unit)."""
+    groups = shape_groups(wl)
+    tiles256 = sum(b * -(-mp // 256) * -(-np_ // 256) for b, mp, np_ in groups)
+    if len(groups) > 1 and tiles256 < 2 * cus:
+        return None
+    out = []
+    for b, mp, np_ in groups:
+        for kind, K in (("gram", np_), ("poly", mp)):
+            if mp >= 1024:
+                t = -(-mp // 256)
+                out.append((kind, (b, mp, np_), b * t * (t + 1) // 2, 16, K // 32, 131072))
+                continue
+            S = mp // 256
+            items = (b * S * (S - 1) // 2 + 3 * (b * S // 4) + (b * S) % 4) if mp % 256 == 0 else 0
+            if mp % 256 == 0 and items >= 2 * cus - cus // 8:
+                out.append((kind, (b, mp, np_), items, 16, K // 32, 131072))
+            else:
+                t = mp // 128
+                out.append((kind, (b, mp, np_), b * t * (t + 1) // 2, 4, K // 32, 65536))
+        tiles = b * -(-mp // 256) * -(-np_ // 256)
+        if 2 * tiles <= cus:
+            out.append(("apply", (b, mp, np_), 4 * tiles, 4, mp // 32, 65536))
+        else:
+            per = -(-tiles // cus)
+            nb = min(cus, (-(-tiles // per) + 7) // 8 * 8)
+            out.append(("apply", (b, mp, np_), nb, 16, per * (mp // 32), 131072))
+    return out
+
+
+def mfma_bound(wl, dev, measured_ns_ms, ns_steps=5, reps=5):
+    """The matrix-core issue bound of the Newton-Schulz products: every product launch of a
+    round (product_launches) replayed by a kernel that issues the same MFMAs per wave on
+    the same grid with no memory traffic (libmuon_mfma_loop.so), timed with HIP events, its
+    shader clock read from per-block timestamps. The sum over a step is the time the products
+    would take if their matrix cores never waited for data at the clock the device then
+    holds; its ratio to the measured product time is the fraction of that bound reached."""
+    import ctypes
+    from orthogonalized_momentum_optimizer_amd import build as b
+    launches = product_launches(wl, torch.cuda.get_device_properties(dev).multi_processor_count)
+    if launches is None or not os.path.exists(b.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.muon_mfma_loop.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3 + [
+        ctypes.POINTER(ctypes.c_float)]
+    lib.muon_mfma_loop.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    rows, total_us = [], 0.0
+    for kind, grp, blocks, nacc, iters, lds in launches:
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        stamps = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+        times = []
+        for _ in range(reps + 1):
+            t = ctypes.c_float(0.0)
+            st = lib.muon_mfma_loop(blocks, nacc, iters, lds, sink.data_ptr(), stamps.data_ptr(),
+                                    ctypes.c_void_p(stream.cuda_stream), ctypes.byref(t))
+            if st != 0:
+                raise RuntimeError(f"muon_mfma_loop failed ({st})")
+            times.append(t.value)
+        us = sorted(times[1:])[len(times[1:]) // 2]
+        sv = stamps.view(blocks, 4).cpu().double()
+        cyc = (sv[:, 1] - sv[:, 0]).median().item()
+        ghz = ((sv[:, 1] - sv[:, 0]) / (sv[:, 3] - sv[:, 2]) * 0.1).median().item()
+        # a 32x32x16 MFMA occupies its SIMD for 32 cycles at the peak rate
+        rows.append({"kind": kind, "group": f"{grp[0]}x{grp[1]}x{grp[2]}", "blocks": blocks,
+                     "tile_per_wave": "128x128" if nacc == 16 else "64x64",
+                     "k_steps_per_wave": iters, "us": us, "clock_ghz": ghz,
+                     "loop_cycles_per_wave": cyc,
+                     "issue_frac": iters * 2 * nacc * 32 / cyc if cyc > 0 else None})
+        total_us += us
+    bound_ms = ns_steps * total_us * 1e-3
+    ns_flops = wl.ns_flops_per_step()
+    return {"launches": rows, "ns_ms_per_step": bound_ms,
+            "ns_frac_of_peak_at_bound": ns_flops / (bound_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "measured_ns_ms_per_step": measured_ns_ms,
+            "frac_of_bound_reached": bound_ms / measured_ns_ms if measured_ns_ms else None}
 
 
 def library_ceiling(wl, dev, apply_tflops, iters=20):
@@ -304,6 +404,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the vendor-library GEMM comparison")
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
+    ap.add_argument("--no-mfma-bound", action="store_true",
+                    help="skip the matrix-core issue bound of the products")
     ap.add_argument("--no-roweq", action="store_true", help="skip the row-equaliser leg")
     ap.add_argument("--adam-only", action="store_true",
                     help="time only the cautious-Adam step and print its JSON object")
@@ -445,6 +547,10 @@ def main():
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                                "traffic": measured_traffic(dom, wl.name),
                                "avg_launch_us": 1e3 * dms / max(dl, 1)}
+
+    if not args.no_mfma_bound and args.precision == "bf16" and "kernels" in out:
+        gemm_ms = sum(out["kernels"][k]["ms_per_step"] for k in ("gram", "poly", "apply"))
+        out["mfma_bound"] = mfma_bound(wl, dev, gemm_ms)
 
     next_rows = {}
     if not args.no_roweq:

@@ -3,7 +3,8 @@
     python -m orthogonalized_momentum_optimizer_amd.build
 
 Every source under csrc/ is compiled with hipcc for gfx950 only and linked into
-orthogonalized_momentum_optimizer_amd/libmuon.so. Objects go to _build/ at the repository
+orthogonalized_momentum_optimizer_amd/libmuon.so, except mfma_loop.hip, a measurement kernel
+for bench.py that goes into libmuon_mfma_loop.so. Objects go to _build/ at the repository
 root. The library links against the HIP runtime by its soname, so inside a process that has
 already loaded PyTorch's HIP runtime the library binds to that same runtime.
 """
@@ -21,6 +22,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
+# measurement only, a library of its own (bench.py's matrix-core issue bound)
+PROBE_LIB = os.path.join(PKG, "libmuon_mfma_loop.so")
+PROBE_SOURCES = ["mfma_loop.hip"]
 
 SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip",
            "ns_quad_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip", "cautious_adam.hip",
@@ -68,13 +72,15 @@ def build(verbose: bool = False) -> str:
             print(msg, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES + PROBE_SOURCES))
+    for lib, part in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp,
+              *part])
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

@@ -81,3 +81,28 @@ def test_cpu_baseline_times_the_oracle_only(monkeypatch):
     assert out["value"] > 2.0, out
     assert "not timed" in out["sample"]
     assert out["kind"] == "oracle" and out["cores"] >= 1
+
+
+def test_product_launch_model_matches_the_launches_of_the_gpt2_124m_set():
+    """The grids the matrix-core bound replays are those the library launches for the
+    GPT-2-124M set on 256 compute units (the kernel trace shows 1008- and 504-block products
+    of 128x128 tiles and 216 persistent apply blocks)."""
+    got = bench.product_launches(si.WORKLOADS["gpt2_124m"], 256)
+    assert got == [
+        ("gram", (48, 768, 768), 1008, 4, 24, 65536),
+        ("poly", (48, 768, 768), 1008, 4, 24, 65536),
+        ("apply", (48, 768, 768), 216, 16, 48, 131072),
+        ("gram", (24, 768, 3072), 504, 4, 96, 65536),
+        ("poly", (24, 768, 3072), 504, 4, 24, 65536),
+        ("apply", (24, 768, 3072), 216, 16, 96, 131072),
+    ]
+    # the apply grids issue exactly the nominal 2 m^2 n flops of their group (every block
+    # takes the same number of 256x256 tiles); the symmetric products one block per upper
+    # 128x128 tile
+    mfma_flops = 2 * 32 * 32 * 16
+    for kind, (b, mp, np_), blocks, nacc, iters, _ in got:
+        if kind == "apply":
+            assert blocks * 4 * iters * 2 * nacc * mfma_flops == 2 * b * mp * mp * np_
+        else:
+            assert blocks == b * (mp // 128) * (mp // 128 + 1) // 2
+    assert bench.product_launches(si.WORKLOADS["gpt2_124m_share8"], 256) is None
