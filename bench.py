@@ -58,7 +58,8 @@ def kind_work(wl, ns_steps=5):
     """Algorithmic work per step of each kernel kind: flops for the products (nominal,
     m <= n: gram 2 m^2 n, poly 2 m^3, apply 2 m^2 n per round), bytes for the elementwise
     kernels (momentum: read G, read+write fp32 M; update: read+write W)."""
-    w = {"gram": 0.0, "poly": 0.0, "apply": 0.0, "momentum": 0.0, "update": 0.0, "norm": 0.0}
+    w = {"gram": 0.0, "poly": 0.0, "apply": 0.0, "momentum": 0.0, "update": 0.0, "norm": 0.0,
+         "rounds": 0.0}
     esz = 2 if wl.dtype == "bf16" else 4
     for r, c in wl.shapes:
         m, n = min(r, c), max(r, c)
@@ -67,7 +68,11 @@ def kind_work(wl, ns_steps=5):
         w["apply"] += ns_steps * 2.0 * m * m * n
         w["momentum"] += r * c * (esz + 8.0)
         w["update"] += r * c * (2.0 * esz)
+    w["rounds"] = w["gram"] + w["poly"] + w["apply"]   # the single-launch rounds
     return w
+
+
+NS_KINDS = ("gram", "poly", "apply", "rounds")
 
 
 def shape_groups(wl):
@@ -81,14 +86,35 @@ def shape_groups(wl):
     return [(b, mp, np_) for (mp, np_), b in sorted(cnt.items())]
 
 
-def product_launches(wl, cus):
-    """Grid, register tile and K steps of every bf16 product launch of one Newton-Schulz
-    round, group by group, as the library launches them (sets whose groups share launches
-    are not modelled: returns None). Each entry: (kind, group, blocks, nacc, iters, lds):
-    blocks of 256 threads, nacc 32x32 accumulator blocks per wave (16: a 128x128 register
-    tile, 4: 64x64), iters 32-deep K steps per wave of the busiest block, lds bytes per
-    block (which sets the blocks per compute unit)."""
+def fused_rounds(groups, ns_steps, cus=256):
+    """Whether the library runs these groups' rounds as one persistent launch (its default
+    where it applies): bf16, 1-16 rounds, at most 4 groups, each 256-aligned with at least 8
+    matrices, a 256-CU device, and at most 8 apply tiles of 256x256 per CU per round."""
+    tiles = sum(b * (mp // 256) * (np_ // 256) for b, mp, np_ in groups)
+    return (1 <= ns_steps <= 16 and 1 <= len(groups) <= 4 and cus == 256 and
+            all(mp % 256 == 0 and np_ % 256 == 0 and b >= 8 for b, mp, np_ in groups) and
+            tiles <= 8 * cus)
+
+
+def product_launches(wl, cus, fused=True, ns_steps=5):
+    """Grid, register tile and K steps of the bf16 product launches, as the library launches
+    them: with the rounds in one persistent launch (fused_rounds), that launch with its
+    K steps dealt evenly over the compute units, group "all" (its entry covers every round);
+    otherwise every product launch of one round, group by group (sets whose groups share
+    launches are not modelled: returns None). Each entry: (kind, group, blocks, nacc, iters,
+    lds): blocks of 256 threads, nacc 32x32 accumulator blocks per wave (16: a 128x128
+    register tile, 4: 64x64), iters 32-deep K steps per wave of the busiest block, lds bytes
+    per block (which sets the blocks per compute unit)."""
     groups = shape_groups(wl)
+    if fused and fused_rounds(groups, ns_steps, cus):
+        # one persistent launch, one block per CU, every round's items and tiles dealt evenly
+        units = 0
+        for b, mp, np_ in groups:
+            S = mp // 256
+            items = b * S * (S - 1) // 2 + 3 * (b * S // 4) + (b * S) % 4
+            units += items * (np_ // 32) + items * (mp // 32)
+            units += b * (mp // 256) * (np_ // 256) * (mp // 32)
+        return [("rounds", "all", cus, 16, -(-units * ns_steps // cus), 131072)]
     tiles256 = sum(b * -(-mp // 256) * -(-np_ // 256) for b, mp, np_ in groups)
     if len(groups) > 1 and tiles256 < 2 * cus:
         return None
@@ -116,7 +142,7 @@ def product_launches(wl, cus):
     return out
 
 
-def mfma_bound(wl, dev, measured_ns_ms, ns_steps=5, reps=5):
+def mfma_bound(wl, dev, measured_ns_ms, ns_steps=5, reps=5, fused=True):
     """The matrix-core issue bound of the Newton-Schulz products: every product launch of a
     round (product_launches) replayed by a kernel that issues the same MFMAs per wave on
     the same grid with no memory traffic (libmuon_mfma_loop.so), timed with HIP events, its
@@ -125,7 +151,8 @@ def mfma_bound(wl, dev, measured_ns_ms, ns_steps=5, reps=5):
     holds; its ratio to the measured product time is the fraction of that bound reached."""
     import ctypes
     from orthogonalized_momentum_optimizer_amd import build as b
-    launches = product_launches(wl, torch.cuda.get_device_properties(dev).multi_processor_count)
+    launches = product_launches(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
+                                fused=fused, ns_steps=ns_steps)
     if launches is None or not os.path.exists(b.PROBE_LIB):
         return None
     lib = ctypes.CDLL(b.PROBE_LIB)
@@ -151,13 +178,15 @@ def mfma_bound(wl, dev, measured_ns_ms, ns_steps=5, reps=5):
         cyc = (sv[:, 1] - sv[:, 0]).median().item()
         ghz = ((sv[:, 1] - sv[:, 0]) / (sv[:, 3] - sv[:, 2]) * 0.1).median().item()
         # a 32x32x16 MFMA occupies its SIMD for 32 cycles at the peak rate
-        rows.append({"kind": kind, "group": f"{grp[0]}x{grp[1]}x{grp[2]}", "blocks": blocks,
+        rows.append({"kind": kind,
+                     "group": grp if isinstance(grp, str) else f"{grp[0]}x{grp[1]}x{grp[2]}",
+                     "blocks": blocks,
                      "tile_per_wave": "128x128" if nacc == 16 else "64x64",
                      "k_steps_per_wave": iters, "us": us, "clock_ghz": ghz,
                      "loop_cycles_per_wave": cyc,
                      "issue_frac": iters * 2 * nacc * 32 / cyc if cyc > 0 else None})
-        total_us += us
-    bound_ms = ns_steps * total_us * 1e-3
+        total_us += us if kind == "rounds" else ns_steps * us
+    bound_ms = total_us * 1e-3
     ns_flops = wl.ns_flops_per_step()
     return {"launches": rows, "ns_ms_per_step": bound_ms,
             "ns_frac_of_peak_at_bound": ns_flops / (bound_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -404,6 +433,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the vendor-library GEMM comparison")
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="one launch per product instead of all rounds in one launch")
     ap.add_argument("--no-mfma-bound", action="store_true",
                     help="skip the matrix-core issue bound of the products")
     ap.add_argument("--no-roweq", action="store_true", help="skip the row-equaliser leg")
@@ -436,7 +467,8 @@ def main():
     W = [si.weight(wl, i).to(dev) for i in range(n)]
     M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in wl.shapes]
     G = [[si.grad(wl, i, t).to(dev) for i in range(n)] for t in range(2)]
-    plan = MuonPlan(wl.shapes, [w.dtype for w in W], [w.dtype for w in W], args.precision, dev)
+    plan = MuonPlan(wl.shapes, [w.dtype for w in W], [w.dtype for w in W], args.precision, dev,
+                    fused=not args.no_fused)
     cfg = make_config()
     stream = torch.cuda.current_stream()
     print(f"[bench] workspace {plan.ws_bytes / 2**20:.1f} MiB; warmup {args.warmup}",
@@ -518,7 +550,7 @@ def main():
             per_step = kms / args.steps
             kernels[k] = {"ms_per_step": per_step, "launches_per_step": launches / args.steps,
                           "avg_launch_us": 1e3 * kms / max(launches, 1)}
-        gemm_ms = sum(prof[k][0] for k in ("gram", "poly", "apply")) / args.steps
+        gemm_ms = sum(prof[k][0] for k in NS_KINDS) / args.steps
         out["kernels"] = kernels
         out["ns_tflops_kernels"] = ns_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
         peak_mm = PEAK_BF16_TFLOPS if args.precision == "bf16" else PEAK_F32_TFLOPS
@@ -534,7 +566,7 @@ def main():
                                 "frac": (ns_ms + ew_ms) / ms}
         dom = max(prof, key=lambda k: prof[k][0])
         dms, dl = prof[dom]
-        if dom in ("gram", "poly", "apply"):
+        if dom in NS_KINDS:
             ach = work[dom] * args.steps / (dms * 1e-3) / 1e12
             out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak_mm,
                                "unit": "TFLOP/s", "frac": ach / peak_mm,
@@ -549,8 +581,8 @@ def main():
                                "avg_launch_us": 1e3 * dms / max(dl, 1)}
 
     if not args.no_mfma_bound and args.precision == "bf16" and "kernels" in out:
-        gemm_ms = sum(out["kernels"][k]["ms_per_step"] for k in ("gram", "poly", "apply"))
-        out["mfma_bound"] = mfma_bound(wl, dev, gemm_ms)
+        gemm_ms = sum(out["kernels"][k]["ms_per_step"] for k in NS_KINDS)
+        out["mfma_bound"] = mfma_bound(wl, dev, gemm_ms, fused=not args.no_fused)
 
     next_rows = {}
     if not args.no_roweq:

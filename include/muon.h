@@ -181,6 +181,21 @@ int muon_newton_schulz(muon_plan *plan, const void *const *in, void *const *out,
 
 void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
 
+/* Whether steps on this plan run all Newton-Schulz rounds as one persistent launch (enable 1,
+ * the default of a new plan) where the plan allows it, or one launch per product (0). The
+ * single launch takes bf16 rounds (at most 16 of them) of plans with at most 4 shape groups,
+ * each a multiple of 256 on both sides with at least 8 matrices, of at most 8 apply tiles of
+ * 256x256 per compute unit per round, on a 256-CU device (8 XCDs): e.g. the GPT-2-124M set,
+ * 48 x 768x768 and 24 x 768x3072. It computes the same products in the same order with the
+ * same instructions, so results are bitwise those of the per-product launches; it deals each
+ * group's matrices to the device's 8 XCDs and runs every item of a matrix on that matrix's
+ * XCD, starting each product of a matrix as soon as the products it reads are complete, with
+ * no launch boundary between rounds. Its workspace (queue and completion counters) is part of
+ * muon_plan_workspace_size. MUON_ERR_INVALID_ARG for a NULL plan or another value of enable.
+ * Steps of a plan whose single launch is on must not overlap on one device with other steps
+ * of the same plan (they share its counters, as they share the rest of its workspace). */
+int muon_plan_set_fused(muon_plan *plan, int enable);
+
 /* Upper bound of muon_plan_set_concurrency's stream count. */
 #define MUON_MAX_STREAMS 4
 
@@ -219,7 +234,8 @@ typedef enum {
   MUON_KERNEL_APPLY = 4,    /* X' = s (a X + B X)                             */
   MUON_KERNEL_UPDATE = 5,   /* W -= lr O (and O out)                          */
   MUON_KERNEL_ROWEQ = 6,    /* row equaliser: row sums of O^2, per-row factors */
-  MUON_KERNEL_KINDS = 7
+  MUON_KERNEL_ROUNDS = 7,   /* all rounds (gram, poly, apply) as one launch    */
+  MUON_KERNEL_KINDS = 8
 } muon_kernel_kind;
 
 /* Waits for the recorded events and writes, per kind (up to nkinds entries), the summed

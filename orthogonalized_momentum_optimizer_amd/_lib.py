@@ -27,14 +27,14 @@ MUON_DT_F32 = 1
 MUON_NS_BF16 = 0
 MUON_NS_F32_DEBUG = 1
 
-KERNEL_KINDS = ("momentum", "norm", "gram", "poly", "apply", "update", "roweq")
+KERNEL_KINDS = ("momentum", "norm", "gram", "poly", "apply", "update", "roweq", "rounds")
 
 EXPORTED = (
     "muon_config_default", "muon_plan_create", "muon_plan_workspace_size", "muon_step",
     "muon_newton_schulz", "muon_plan_destroy", "muon_plan_set_profiling",
     "muon_plan_read_profile", "muon_status_string", "muon_last_error",
     "muon_adam_config_default", "muon_cautious_adam_step", "muon_step_noalloc",
-    "muon_plan_set_concurrency",
+    "muon_plan_set_concurrency", "muon_plan_set_fused",
 )
 MUON_MAX_STREAMS = 4
 MUON_STATIC_SCRATCH_BYTES = 64 << 20
@@ -137,6 +137,8 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_set_profiling.restype = ctypes.c_int
     L.muon_plan_set_concurrency.argtypes = [vp, ctypes.c_int]
     L.muon_plan_set_concurrency.restype = ctypes.c_int
+    L.muon_plan_set_fused.argtypes = [vp, ctypes.c_int]
+    L.muon_plan_set_fused.restype = ctypes.c_int
     L.muon_plan_read_profile.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(i64), ctypes.c_int]
     L.muon_plan_read_profile.restype = ctypes.c_int
@@ -224,6 +226,10 @@ def muon_plan_set_profiling(plan: int, enable: bool) -> None:
 
 def muon_plan_set_concurrency(plan: int, streams: int) -> None:
     _check(lib().muon_plan_set_concurrency(plan, int(streams)))
+
+
+def muon_plan_set_fused(plan: int, enable: bool) -> None:
+    _check(lib().muon_plan_set_fused(plan, 1 if enable else 0))
 
 
 def muon_plan_read_profile(plan: int) -> dict:

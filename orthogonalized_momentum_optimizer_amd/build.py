@@ -27,8 +27,8 @@ PROBE_LIB = os.path.join(PKG, "libmuon_mfma_loop.so")
 PROBE_SOURCES = ["mfma_loop.hip"]
 
 SOURCES = ["plan.hip", "elementwise.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip",
-           "ns_quad_bf16.hip", "ns_apply_bf16.hip", "ns_gemm_f32.hip", "cautious_adam.hip",
-           "noalloc.hip"]
+           "ns_quad_bf16.hip", "ns_apply_bf16.hip", "ns_fused_bf16.hip", "ns_gemm_f32.hip",
+           "cautious_adam.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -118,6 +118,13 @@ hipError_t launch_quad_bf16(const NsGroup* const* groups, int n, int mode, float
                             float c, hipStream_t s);
 hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, float c,
                                hipStream_t s);
+// All rounds of a step as one persistent launch (ns_fused_bf16.hip): groups' X_0 in x_in,
+// the result after `rounds` rounds in x_in for even rounds and x_out for odd; abc holds the
+// rounds' (a, b, c); sync: fused_sync_words 4-byte words of workspace (cleared by the launch).
+bool fused_rounds_ok(const NsGroup* groups, int n, int rounds);
+size_t fused_sync_words(const NsGroup* groups, int n, int rounds);
+hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
+                             uint32_t* sync, hipStream_t s);
 // fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip): B = bA + cAA and
 // X' = s1 (aX + BX), the round as written
 hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);

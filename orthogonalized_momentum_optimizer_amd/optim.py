@@ -60,10 +60,11 @@ class MuonPlan:
     def __init__(self, shapes: Sequence[Sequence[int]], param_dtypes: Sequence[torch.dtype],
                  grad_dtypes: Sequence[torch.dtype], precision: str = "bf16",
                  device: Optional[torch.device] = None, workspace: bool = True,
-                 streams: int = L.MUON_MAX_STREAMS):
+                 streams: int = L.MUON_MAX_STREAMS, fused: bool = True):
         """``workspace=False``: no workspace is allocated; only ``step_noalloc`` (the
         library's static device scratch) can then run the step. ``streams``: shape groups a
-        step may run concurrently (muon_plan_set_concurrency; 1 runs them in sequence)."""
+        step may run concurrently (muon_plan_set_concurrency; 1 runs them in sequence).
+        ``fused``: all rounds as one launch where the plan allows it (muon_plan_set_fused)."""
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.pdt = [dtype_code(d) for d in param_dtypes]
         self.gdt = [dtype_code(d) for d in grad_dtypes]
@@ -79,11 +80,15 @@ class MuonPlan:
             assert self.workspace.data_ptr() % 256 == 0
         self._mats = None
         self._mats_key = None
+        L.muon_plan_set_fused(self.handle, fused)
         with torch.cuda.device(dev):
             L.muon_plan_set_concurrency(self.handle, streams)
 
     def set_concurrency(self, streams: int):
         L.muon_plan_set_concurrency(self.handle, streams)
+
+    def set_fused(self, enable: bool):
+        L.muon_plan_set_fused(self.handle, enable)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -1,5 +1,5 @@
-// Host check of the four-block item map of ns_quad_bf16.hip (compiled into this program with
-// the library's flags): for a range of group sizes, every upper block (r <= c) of every
+// Host check of the four-block item map of ns_quad_item.h (compiled into this program with
+// ns_quad_bf16.hip, the library's flags): for a range of group sizes, every upper block (r <= c) of every
 // matrix is computed and stored by exactly one wave, every index is in range, and the data a
 // wave multiplies is what the waves of its item load (slot sa holds the block's row panel,
 // slot sb its column panel, both of the block's matrix). Prints "quad items ok".
@@ -13,7 +13,7 @@ thread_local LaunchTiming g_launch_timing;  // referenced by launch_k, unused he
 int device_cus() { return 256; }
 }  // namespace muon
 
-using muon::QuadArgs;
+using muon::quad::QuadItems;
 
 static int fails = 0;
 #define CHECK(c, ...)                         \
@@ -27,31 +27,26 @@ int main() {
   long long checked = 0;
   for (int mp = 256; mp <= 2048; mp += 256) {
     for (int batch = 1; batch <= 50; ++batch) {
-      QuadArgs g{};
-      g.mp = mp;
-      g.S = mp / 256;
-      g.pairs_per_mat = g.S * (g.S - 1) / 2;
-      g.pair_items = batch * g.pairs_per_mat;
-      g.triples = batch * g.S;
+      const QuadItems g = muon::quad::quad_items_of(batch, mp);
       const int T = mp / 128;
-      const int items = muon::quad_item_count(g.pair_items, g.triples);
+      const int items = muon::quad::quad_item_count(g);
       muon::NsGroup G{};
       G.mp = mp;
       G.batch = batch;
       CHECK(muon::quad_items(G) == items, "mp %d batch %d: item counts differ\n", mp, batch);
       std::vector<int> hits((size_t)batch * T * T, 0);
       for (int L = 0; L < items; ++L) {
-        muon::QuadWave w[4];
-        for (int k = 0; k < 4; ++k) w[k] = muon::quad_wave(g, L, k);
+        muon::quad::QuadWave w[4];
+        for (int k = 0; k < 4; ++k) w[k] = muon::quad::quad_wave(g, L, k);
         for (int k = 0; k < 4; ++k) {
-          const muon::QuadWave& q = w[k];
+          const muon::quad::QuadWave& q = w[k];
           CHECK(q.lmat >= 0 && q.lmat < batch && q.lpan >= 0 && q.lpan < T,
                 "mp %d batch %d item %d wave %d: load slot out of range\n", mp, batch, L, k);
           CHECK(q.sa >= 0 && q.sa < 4 && q.sb >= 0 && q.sb < 4,
                 "mp %d batch %d item %d wave %d: slot index out of range\n", mp, batch, L, k);
           if (q.sa < 0 || q.sa > 3 || q.sb < 0 || q.sb > 3) continue;
-          const muon::QuadWave& ra = w[q.sa];
-          const muon::QuadWave& rb = w[q.sb];
+          const muon::quad::QuadWave& ra = w[q.sa];
+          const muon::quad::QuadWave& rb = w[q.sb];
           CHECK(ra.lmat == q.omat && ra.lpan == q.rpan,
                 "mp %d batch %d item %d wave %d: row slot holds the wrong panel\n", mp, batch, L, k);
           CHECK(rb.lmat == q.omat && rb.lpan == q.cpan,

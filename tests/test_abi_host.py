@@ -59,7 +59,9 @@ def test_status_strings():
 def _ws_expected(shapes, esz):
     """Workspace layout: per padded wide group X0, X1 (count*mp*np), A, B (count*mp*mp),
     partial sums (count * 64x64 tiles of X, doubles), scales (16 B per matrix), partial row sums and
-    row factors of the row equaliser (count*8*np and count*np floats), each 256-aligned."""
+    row factors of the row equaliser (count*8*np and count*np floats), each 256-aligned; then
+    the single-launch rounds' queues, flag and completion counters (8 x 16 + 16 words and 3 x 16
+    rounds x count words per group, 4 bytes each)."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     groups = {}
     for r, c in shapes:
@@ -76,6 +78,8 @@ def _ws_expected(shapes, esz):
         tot = al(tot + cnt * 16)
         tot = al(tot + cnt * 8 * np_ * 4)
         tot = al(tot + cnt * np_ * 4)
+    if groups:
+        tot = al(tot + 4 * (8 * 16 + 16 + sum(3 * 16 * cnt for cnt in groups.values())))
     return tot
 
 

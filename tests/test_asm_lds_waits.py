@@ -5,7 +5,8 @@ import pytest
 import asm_check
 from orthogonalized_momentum_optimizer_amd import build
 
-KERNEL_SOURCES = ["ns_apply_bf16.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip", "ns_quad_bf16.hip"]
+KERNEL_SOURCES = ["ns_apply_bf16.hip", "ns_gemm_bf16.hip", "ns_sym256_bf16.hip", "ns_quad_bf16.hip",
+                  "ns_fused_bf16.hip"]
 
 
 @pytest.mark.parametrize("src", KERNEL_SOURCES)

@@ -87,7 +87,7 @@ def test_product_launch_model_matches_the_launches_of_the_gpt2_124m_set():
     """The grids the matrix-core bound replays are those the library launches for the
     GPT-2-124M set on 256 compute units (the kernel trace shows 1008- and 504-block products
     of 128x128 tiles and 216 persistent apply blocks)."""
-    got = bench.product_launches(si.WORKLOADS["gpt2_124m"], 256)
+    got = bench.product_launches(si.WORKLOADS["gpt2_124m"], 256, fused=False)
     assert got == [
         ("gram", (48, 768, 768), 1008, 4, 24, 65536),
         ("poly", (48, 768, 768), 1008, 4, 24, 65536),
@@ -106,3 +106,13 @@ def test_product_launch_model_matches_the_launches_of_the_gpt2_124m_set():
         else:
             assert blocks == b * (mp // 128) * (mp // 128 + 1) // 2
     assert bench.product_launches(si.WORKLOADS["gpt2_124m_share8"], 256) is None
+    # all rounds in one launch: 252 + 126 four-block items of K = 768 / 3072 (Gram) and
+    # 768 (polynomial), 432 + 864 apply tiles of K = 768, five rounds over 256 blocks
+    units = 252 * (24 + 24) + 432 * 24 + 126 * (96 + 24) + 864 * 24
+    assert bench.product_launches(si.WORKLOADS["gpt2_124m"], 256) == [
+        ("rounds", "all", 256, 16, -(-5 * units // 256), 131072)]
+    # sets with more than 8 apply tiles per compute unit per round keep one launch per
+    # product: the tall stress set (96 x 768x3072 wide, 13.5 tiles per unit)
+    assert bench.fused_rounds(bench.shape_groups(si.WORKLOADS["tall_stress"]), 5) is False
+    assert bench.fused_rounds(bench.shape_groups(si.WORKLOADS["gpt2_124m"]), 5) is True
+    assert bench.fused_rounds(bench.shape_groups(si.WORKLOADS["gpt2_124m"]), 5, cus=304) is False

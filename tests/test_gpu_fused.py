@@ -1,0 +1,80 @@
+"""All Newton-Schulz rounds as one persistent launch (muon_plan_set_fused, on by default).
+It computes the per-product kernels' products in their order with their instructions, so a
+step with it must give bitwise the W, momentum and O of the same step with one launch per
+product; parity with the oracle over whole trajectories is in test_gpu_trajectories.py (the
+GPT-2-124M and tall-stress sets take this launch by default). Round counts 1 and 2 check the
+ping-pong of X (the result lands in either buffer), 16 the largest the launch takes; a
+per-round coefficient table checks that each round reads its own (a, b, c)."""
+import pytest
+import torch
+
+import seeded_inputs as si
+from orthogonalized_momentum_optimizer_amd import MuonPlan, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+# three shape groups of 8 matrices, 256-aligned: 256x256, 512x256 (tall, runs as 256x512) and
+# 256x1024; with 8 matrices per group every XCD holds one matrix of each
+SMALL = [(256, 256)] * 8 + [(512, 256)] * 8 + [(256, 1024)] * 8
+
+
+def _error_flag(plan, wl):
+    """The single launch's error flag (set when a wait for a matrix's inputs gave up): the
+    workspace ends with its queues (8 x 16 words), the flag, 15 spare words and the completion
+    counters (3 x 16 rounds words per matrix), 256-byte aligned."""
+    words = 8 * 16 + 16 + 3 * 16 * wl.n
+    off = plan.ws_bytes - (4 * words + 255) // 256 * 256
+    return int(plan.workspace[off + 512:off + 516].cpu().view(torch.int32)[0])
+
+
+def _steps(wl, fused, cfg, steps):
+    plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16", dev(),
+                    fused=fused)
+    W = [si.weight(wl, i).to(dev()) for i in range(wl.n)]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+    O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+    for t in range(steps):
+        G = [si.grad(wl, i, t).to(dev()) for i in range(wl.n)]
+        plan.step(W, G, M, cfg, outs=O)
+        torch.cuda.synchronize()
+        if fused:
+            assert _error_flag(plan, wl) == 0, f"step {t}: a wait of the single launch gave up"
+    out = [x.clone() for x in W + M + O]
+    plan.close()
+    return out
+
+
+def _assert_bitwise(a, b, what):
+    bad = [i for i, (x, y) in enumerate(zip(a, b)) if not torch.equal(x, y)]
+    assert not bad, f"{what}: buffers {bad[:10]} differ between the single launch and per-product launches"
+
+
+@pytest.mark.parametrize("ns_steps", [1, 2, 5, 16])
+def test_single_launch_rounds_equal_per_product_launches(ns_steps):
+    print(f"[fused] small set, ns_steps={ns_steps}", flush=True)
+    wl = si.custom(SMALL, steps=2, cfg_id=150 + ns_steps)
+    cfg = make_config(ns_steps=ns_steps)
+    _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), f"ns_steps {ns_steps}")
+
+
+def test_single_launch_rounds_with_a_coefficient_table():
+    print("[fused] small set, per-round coefficients", flush=True)
+    wl = si.custom(SMALL, steps=2, cfg_id=170)
+    g = torch.Generator().manual_seed(170)
+    u = (torch.rand(5, 3, generator=g) * 2 - 1).tolist()
+    # a different (a, b, c) every round, of the size of the fixed map's
+    table = [(3.0 + 0.5 * a, -4.5 + 0.5 * b, 2.0 + 0.25 * c) for a, b, c in u]
+    cfg = make_config(schedule=table)
+    _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), "schedule")
+
+
+def test_single_launch_rounds_gpt2_124m_bitwise():
+    print("[fused] gpt2_124m, 2 steps", flush=True)
+    wl = si.WORKLOADS["gpt2_124m"]
+    cfg = make_config()
+    _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), "gpt2_124m")
