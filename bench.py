@@ -247,30 +247,33 @@ def library_ceiling(wl, dev, apply_tflops, iters=20):
             "apply_kernel_over_gemm_8192": apply_tflops / big_tf if apply_tflops else None}
 
 
-KERNEL_SOURCES = {   # kernel kind -> the source file that defines its bf16 kernel
-    "apply": "ns_apply_bf16.hip", "gram": "ns_gemm_bf16.hip", "poly": "ns_gemm_bf16.hip",
-    "momentum": "elementwise.hip", "update": "elementwise.hip", "norm": "elementwise.hip",
-    "cautious_adam": "cautious_adam.hip",
+KERNEL_SOURCES = {   # kernel kind -> the source files that define its bf16 kernel
+    "apply": ("ns_apply_bf16.hip",), "gram": ("ns_gemm_bf16.hip",),
+    "poly": ("ns_gemm_bf16.hip",), "rounds": ("ns_fused_bf16.hip", "ns_quad_item.h"),
+    "momentum": ("elementwise.hip",), "update": ("elementwise.hip",),
+    "norm": ("elementwise.hip",), "cautious_adam": ("cautious_adam.hip",),
 }
 
 
 def measured_traffic(kind, workload):
     """HBM bytes per launch of a kernel kind, from the rocprofv3 counter summary committed
     under profiles/ (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy of known
-    size). None when there is no summary or the kernel's source changed since it was taken."""
+    size). None when there is no summary or the kernel's sources changed since it was taken
+    (the summary holds the SHA-256 of its source files concatenated in KERNEL_SOURCES order)."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.md")
-    src = os.path.join(ROOT, "orthogonalized_momentum_optimizer_amd", "csrc",
-                       KERNEL_SOURCES.get(kind, ""))
-    if not os.path.exists(path) or not os.path.exists(src):
+    srcs = [os.path.join(ROOT, "orthogonalized_momentum_optimizer_amd", "csrc", f)
+            for f in KERNEL_SOURCES.get(kind, ())]
+    if not os.path.exists(path) or not srcs or not all(os.path.exists(f) for f in srcs):
         return None
     text = open(path).read()
     m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     m_h = re.search(r"^source_sha256:\s*([0-9a-f]+)", text, re.M)
     if not m_b or not m_h:
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+    if digest != m_h.group(1):
         return None
     return float(m_b.group(1))
 

@@ -21,6 +21,9 @@ def dev():
 # three shape groups of 8 matrices, 256-aligned: 256x256, 512x256 (tall, runs as 256x512) and
 # 256x1024; with 8 matrices per group every XCD holds one matrix of each
 SMALL = [(256, 256)] * 8 + [(512, 256)] * 8 + [(256, 1024)] * 8
+# two groups of 768-row matrices (the GPT-2-124M widths at a sixth of its count): 768x768 and
+# 1536x768 (tall, runs as 768x1536)
+MID = [(768, 768)] * 8 + [(1536, 768)] * 8
 
 
 def _error_flag(plan, wl):
@@ -60,6 +63,14 @@ def test_single_launch_rounds_equal_per_product_launches(ns_steps):
     wl = si.custom(SMALL, steps=2, cfg_id=150 + ns_steps)
     cfg = make_config(ns_steps=ns_steps)
     _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), f"ns_steps {ns_steps}")
+
+
+@pytest.mark.parametrize("ns_steps", [1, 3, 5])
+def test_single_launch_768_rows_equal_per_product_launches(ns_steps):
+    print(f"[fused] 768-row set, ns_steps={ns_steps}", flush=True)
+    wl = si.custom(MID, steps=3, cfg_id=160 + ns_steps)
+    cfg = make_config(ns_steps=ns_steps)
+    _assert_bitwise(_steps(wl, True, cfg, 3), _steps(wl, False, cfg, 3), f"ns_steps {ns_steps}")
 
 
 def test_single_launch_rounds_with_a_coefficient_table():
