@@ -16,11 +16,20 @@ def dev():
     return torch.device("cuda", 0)
 
 
-@pytest.mark.parametrize("row_equalize", [False, True])
-def test_muon_step_graph_replay_bitwise(row_equalize):
-    print(f"[graph] muon step, row_equalize={row_equalize}", flush=True)
-    wl = si.custom([(200, 328), (328, 200), (768, 768), (768, 3072), (3072, 768), (5, 3)],
-                   steps=4, cfg_id=130)
+# a ragged set (one launch per product) and a set whose rounds run as one persistent launch
+# (three 256-aligned groups of 8 matrices; its queue and counters are cleared by a kernel of
+# the captured sequence on every replay)
+SETS = {
+    "ragged": [(200, 328), (328, 200), (768, 768), (768, 3072), (3072, 768), (5, 3)],
+    "single_launch": [(256, 256)] * 8 + [(512, 256)] * 8 + [(256, 1024)] * 8,
+}
+
+
+@pytest.mark.parametrize("row_equalize,shapes", [(False, "ragged"), (True, "ragged"),
+                                                 (False, "single_launch")])
+def test_muon_step_graph_replay_bitwise(row_equalize, shapes):
+    print(f"[graph] muon step, {shapes} set, row_equalize={row_equalize}", flush=True)
+    wl = si.custom(SETS[shapes], steps=4, cfg_id=130 if shapes == "ragged" else 131)
     plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16", dev())
     cfg = make_config(row_equalize=row_equalize)
     grads = [[si.grad(wl, i, t).to(dev()) for i in range(wl.n)] for t in range(wl.steps)]

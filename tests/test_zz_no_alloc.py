@@ -69,3 +69,13 @@ def test_noalloc_row_equalizer_matches_step():
     cfg = make_config(row_equalize=True)
     print("[gpu] noalloc: row equaliser", flush=True)
     _same(_run(wl, 2, False, cfg, row_eq=True), _run(wl, 2, True, cfg, row_eq=True), "roweq")
+
+
+def test_noalloc_single_launch_rounds_match_step():
+    """A set that takes the single-launch rounds (three 256-aligned groups of 8 matrices, 20.5
+    MiB of scratch): its queues and completion counters then live in the static scratch and
+    are cleared by the launch's own clearing kernel on every call."""
+    wl = si.custom([(256, 256)] * 8 + [(512, 256)] * 8 + [(256, 1024)] * 8, dtype="bf16",
+                   steps=2, cfg_id=152)
+    print("[gpu] noalloc: single-launch rounds", flush=True)
+    _same(_run(wl, 2, False), _run(wl, 2, True), "single-launch rounds")
