@@ -89,3 +89,29 @@ def test_single_launch_rounds_gpt2_124m_bitwise():
     wl = si.WORKLOADS["gpt2_124m"]
     cfg = make_config()
     _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), "gpt2_124m")
+
+
+def test_single_launch_newton_schulz_entry():
+    """muon_newton_schulz (rounds only, no momentum or update) on a set that takes the single
+    launch: bitwise the per-product launches' output, and within the bf16 tolerance of the
+    oracle's orthogonalisation on one matrix of each group."""
+    import numpy as np
+    import oracle
+    print("[fused] newton_schulz entry, small set", flush=True)
+    wl = si.custom(SMALL, cfg_id=175)
+    X = [si.grad(wl, i, 0).to(dev()) for i in range(wl.n)]
+    outs = []
+    for fused in (True, False):
+        Y = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+        plan = MuonPlan(wl.shapes, [torch.float32] * wl.n, [x.dtype for x in X], "bf16", dev(),
+                        fused=fused)
+        plan.newton_schulz(X, Y, make_config(ns_steps=5))
+        torch.cuda.synchronize()
+        plan.close()
+        outs.append(Y)
+    _assert_bitwise(outs[0], outs[1], "newton_schulz")
+    for i in (0, 8, 16):
+        ref, _ = oracle.orthogonalize(X[i].double().cpu().numpy(), 5)
+        got = outs[0][i].double().cpu().numpy()
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= 3e-2, (i, err)
