@@ -193,7 +193,13 @@ void muon_plan_destroy(muon_plan *plan); /* NULL is ignored */
  * no launch boundary between rounds. Its workspace (queue and completion counters) is part of
  * muon_plan_workspace_size. MUON_ERR_INVALID_ARG for a NULL plan or another value of enable.
  * Steps of a plan whose single launch is on must not overlap on one device with other steps
- * of the same plan (they share its counters, as they share the rest of its workspace). */
+ * of the same plan (they share its counters, as they share the rest of its workspace).
+ * Failure: a work item waits for the items it reads with a bounded poll (by default 2^22
+ * polls, a few seconds, which correct operation never approaches; the environment variable
+ * MUON_FUSED_MAX_POLLS, read when a plan is created, sets another count, and 0 makes every
+ * wait give up at once, which tests the failure path). A wait that gives up
+ * marks the launch failed, and the step's update then writes NaN to every W and O of the plan,
+ * so a device that stalls the launch cannot leave silently wrong parameters. */
 int muon_plan_set_fused(muon_plan *plan, int enable);
 
 /* Upper bound of muon_plan_set_concurrency's stream count. */

@@ -356,7 +356,9 @@ __global__ __launch_bounds__(256) void update_kernel(ElemLaunch L) {
   const void* x = static_cast<const char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
   void* w = L.param[q];
   void* o = L.out[q];
-  const float s = L.apply_scale ? L.scales[4 * q] : 1.f;
+  // a failed single launch of the rounds (L.fault set) makes O, and so W, NaN
+  const float s = (L.fault && *L.fault != 0u) ? __builtin_nanf("")
+                  : L.apply_scale ? L.scales[4 * q] : 1.f;
   const float lr = L.lr;
   const float* rowf = L.rowf ? L.rowf + (size_t)q * L.np : nullptr;
 
@@ -458,7 +460,9 @@ __global__ __launch_bounds__(256) void update_kernel8(ElemLaunch L) {
   const void* x = static_cast<const char*>(L.x) + (size_t)q * L.mp * L.np * (XDT == 0 ? 2 : 4);
   void* w = L.param[q];
   void* o = L.out[q];
-  const float s = L.apply_scale ? L.scales[4 * q] : 1.f;
+  // a failed single launch of the rounds (L.fault set) makes O, and so W, NaN
+  const float s = (L.fault && *L.fault != 0u) ? __builtin_nanf("")
+                  : L.apply_scale ? L.scales[4 * q] : 1.f;
   const float lr = L.lr;
   const float* rowf = L.rowf ? L.rowf + (size_t)q * L.np : nullptr;
 

@@ -67,6 +67,7 @@ struct ElemLaunch {
                                    // per row, np floats each, per slot)
   float* rowf;                     // finish: out; update: per-row factor of O
   float row_beta, row_eps;
+  const uint32_t* fault;           // update: nonzero word = the step's rounds failed (O := NaN)
 };
 
 // dtype codes: 0 = bf16, 1 = f32 (match muon_dtype)
@@ -124,7 +125,9 @@ hipError_t launch_poly256_bf16(const NsGroup* groups, int n, float a, float b, f
 bool fused_rounds_ok(const NsGroup* groups, int n, int rounds);
 size_t fused_sync_words(const NsGroup* groups, int n, int rounds);
 hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
-                             uint32_t* sync, hipStream_t s);
+                             uint32_t* sync, int max_polls, hipStream_t s);
+// The word of a fused launch's sync area that is nonzero once one of its waits gave up.
+inline uint32_t* fused_error_word(uint32_t* sync) { return sync + 8 * 16; }
 // fp32 storage and arithmetic, the debug precision (ns_gemm_f32.hip): B = bA + cAA and
 // X' = s1 (aX + BX), the round as written
 hipError_t launch_gram_f32(const NsGroup& g, hipStream_t s);

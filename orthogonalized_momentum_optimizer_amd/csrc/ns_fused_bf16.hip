@@ -29,10 +29,12 @@
 // Progress. Items are taken in queue order and an item waits only for items earlier in its
 // XCD's queue, each already taken by a running block that waits only for earlier items in
 // turn, so the earliest unfinished item never waits and every wait ends. Each wait also
-// gives up after kMaxPolls polls (about half a second), sets the error flag, which ends every
-// later wait at once, and goes on, so no wave can spin for long whatever happens; and no
-// block makes more passes than the queue has items. Counters, queues and the flag are zeroed
-// by a small kernel before the launch.
+// gives up after max_polls polls (the plan's default, 2^22, is a few seconds), sets the error
+// flag, which ends every later wait at once, and goes on, so no wave can spin for long
+// whatever happens; and no block makes more passes than the queue has items. A step whose
+// launch set the flag makes its update write NaN to every W and O (the update kernels read
+// the flag), so such a failure cannot pass unnoticed. Counters, queues and the flag are
+// zeroed by a small kernel before the launch.
 #include <algorithm>
 #include <vector>
 
@@ -48,7 +50,6 @@ using quad::kUnitsStage;
 
 constexpr int kFusedMaxGroups = 4;
 constexpr int kFusedMaxRounds = 16;
-constexpr int kMaxPolls = 1 << 19;  // ~0.5 s of polling
 enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_APPLY = 2 };
 
 struct FusedGroup {
@@ -70,6 +71,7 @@ struct FusedLaunch {
   float coef[kFusedMaxRounds][3];    // (a, b, c) of each round
   uint32_t* queue;                   // per-XCD item counters, 64 bytes apart
   uint32_t* err;                     // 1 once a wait gave up
+  int max_polls;                     // polls after which a wait gives up
 };
 
 // ---- the apply tile ----
@@ -289,15 +291,21 @@ __device__ __forceinline__ int phase_items(const FusedGroup& G, int ph, int x) {
 // the L2 performs and answers: a plain load could keep returning a copy cached in the L1).
 // Once any wait of the launch has given up, the flag makes every later wait return at once,
 // so a launch whose counters never complete still ends within about one poll limit.
-__device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target, uint32_t* err) {
+// max_polls 0 gives up at once, whatever the count (the failure path, for a test).
+__device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target, uint32_t* err,
+                                           int max_polls) {
   if ((threadIdx.x & 63) != 0) return;
+  if (max_polls == 0) {
+    atomicOr(err, 1u);
+    return;
+  }
   int polls = 0;
   while (__hip_atomic_fetch_add(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if ((polls & 1023) == 0 &&
         __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
       break;
     __builtin_amdgcn_s_sleep(2);
-    if (++polls >= kMaxPolls) {
+    if (++polls >= max_polls) {
       atomicOr(err, 1u);
       break;
     }
@@ -374,20 +382,20 @@ __global__ __launch_bounds__(256) void ns_fused_bf16(FusedLaunch) {
         if (it.ph == PH_APPLY) {
           const int j = it.i / (G.tiles_m * G.tiles_n);
           wait_count(G.cnt + ((size_t)PH_POLY * F.rounds + it.r) * row + (x + 8 * j), G.nblk,
-                     F.err);
+                     F.err, F.max_polls);
         } else {
           const quad::QuadItems qi = quad::quad_items_of(local_batch(G.batch, x), G.mp);
           const int m0 = x + 8 * quad::quad_wave(qi, it.i, 0).lmat;
           const int m2 = x + 8 * quad::quad_wave(qi, it.i, 3).lmat;
           if (it.ph == PH_POLY) {
             uint32_t* c = G.cnt + ((size_t)PH_GRAM * F.rounds + it.r) * row;
-            wait_count(c + m0, G.nblk, F.err);
-            wait_count(c + m2, G.nblk, F.err);
+            wait_count(c + m0, G.nblk, F.err, F.max_polls);
+            wait_count(c + m2, G.nblk, F.err, F.max_polls);
           } else if (it.r > 0) {
             uint32_t* c = G.cnt + ((size_t)PH_APPLY * F.rounds + it.r - 1) * row;
             const uint32_t tiles4 = 4u * G.tiles_m * G.tiles_n;
-            wait_count(c + m0, tiles4, F.err);
-            wait_count(c + m2, tiles4, F.err);
+            wait_count(c + m0, tiles4, F.err, F.max_polls);
+            wait_count(c + m2, tiles4, F.err, F.max_polls);
           }
         }
         asm volatile("buffer_inv sc0" ::: "memory");
@@ -475,14 +483,15 @@ size_t fused_sync_words(const NsGroup* groups, int n, int rounds) {
 }
 
 hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
-                             uint32_t* sync, hipStream_t s) {
+                             uint32_t* sync, int max_polls, hipStream_t s) {
   FusedLaunch F{};
   F.ng = n;
   F.rounds = rounds;
+  F.max_polls = max_polls;
   for (int r = 0; r < rounds; ++r)
     for (int c = 0; c < 3; ++c) F.coef[r][c] = abc[3 * r + c];
   F.queue = sync;
-  F.err = sync + 8 * 16;
+  F.err = fused_error_word(sync);
   uint32_t* cnt = sync + 8 * 16 + 16;
   for (int k = 0; k < n; ++k) {
     const NsGroup& G = groups[k];

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -89,6 +90,7 @@ struct muon_plan {
   size_t ws_bytes = 0;
   size_t off_sync = 0;   // the fused rounds' counters (kFusedSyncRounds rounds)
   bool fused = true;     // muon_plan_set_fused
+  int fused_max_polls = 1 << 22;  // MUON_FUSED_MAX_POLLS when the plan was made
   // last argument set that passed the overlap check
   std::vector<muon_matrix> checked_mats;
   std::vector<const void*> checked_ptrs;
@@ -357,6 +359,8 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
     return res;
   };
 
+  // the single launch's error word (set: its rounds failed, and the update writes NaN)
+  const uint32_t* fault = nullptr;
   // phase 3: row equaliser (optional), parameter update (and O output) from X = xres
   auto finish = [&](const Group& G, char* xres, hipStream_t stream) {
     float* scales = scales_of(G);
@@ -410,6 +414,7 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
         E.apply_scale = cfg->ns_steps == 0;
         E.lr = cfg->lr;
         E.rowf = row_vars ? rowf + (size_t)slot * G.np : nullptr;
+        E.fault = fault;
         const int out_dt = out_param_dtype ? (S.pdt == MUON_DT_F32) : 1;
         L.run(MUON_KERNEL_UPDATE, "update",
               [&] { return launch_update(E, S.pdt == MUON_DT_F32, out_dt, f32, stream); });
@@ -440,8 +445,10 @@ int enqueue(muon_plan* p, const void* const* grads, float* const* moms, void* co
                                                                  : (&cfg->a)[c];
     uint32_t* sync = reinterpret_cast<uint32_t*>(base + p->off_sync);
     L.run(MUON_KERNEL_ROUNDS, "rounds", [&] {
-      return launch_fused_bf16(N.data(), ng, cfg->ns_steps, abc.data(), sync, stream);
+      return launch_fused_bf16(N.data(), ng, cfg->ns_steps, abc.data(), sync,
+                               p->fused_max_polls, stream);
     });
+    fault = fused_error_word(sync);
     for (int gi = 0; gi < ng; ++gi) {
       const Group& G = p->groups[gi];
       finish(G, base + ((cfg->ns_steps & 1) ? G.off_x1 : G.off_x0), stream);
@@ -595,6 +602,12 @@ int muon_plan_create(muon_plan** out, const int64_t* rows, const int64_t* cols,
     off = align256(off + 4 * words);
   }
   p->ws_bytes = off;
+  // the single launch's wait limit (polls); a test sets it to 0 to exercise the failure path
+  if (const char* e = std::getenv("MUON_FUSED_MAX_POLLS")) {
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (end != e && *end == '\0' && v >= 0 && v <= (1L << 30)) p->fused_max_polls = (int)v;
+  }
 
   *out = p;
   return MUON_OK;

@@ -115,3 +115,31 @@ def test_single_launch_newton_schulz_entry():
         got = outs[0][i].double().cpu().numpy()
         err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
         assert err <= 3e-2, (i, err)
+
+
+def test_single_launch_failure_makes_the_step_nan(monkeypatch):
+    """The failure path, forced from the host: with MUON_FUSED_MAX_POLLS=0 (read when a plan is
+    made) every wait of the single launch gives up at once, as a stalled device would make it
+    do after its poll limit. The launch still ends (its items compute from whatever their
+    inputs hold, all in bounds), sets its error flag, and the step's update writes NaN to
+    every W and O instead of leaving silently wrong parameters. A plan made afterwards, without
+    the variable, steps normally."""
+    print("[fused] forced failure of the single launch", flush=True)
+    wl = si.custom(SMALL, steps=1, cfg_id=176)
+    cfg = make_config()
+    monkeypatch.setenv("MUON_FUSED_MAX_POLLS", "0")
+    plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16", dev())
+    monkeypatch.delenv("MUON_FUSED_MAX_POLLS")
+    W = [si.weight(wl, i).to(dev()) for i in range(wl.n)]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+    O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+    G = [si.grad(wl, i, 0).to(dev()) for i in range(wl.n)]
+    plan.step(W, G, M, cfg, outs=O)
+    torch.cuda.synchronize()
+    assert _error_flag(plan, wl) != 0
+    assert all(bool(torch.isnan(w).all()) for w in W)
+    assert all(bool(torch.isnan(o).all()) for o in O)
+    plan.close()
+    # the next plan steps normally
+    out = _steps(wl, True, cfg, 1)
+    assert all(bool(torch.isfinite(x).all()) for x in out)
