@@ -8,8 +8,8 @@
 //   apply   X_{r+1} = s1 B' X_r               (256x256 tiles, the apply kernel's tile)
 //
 // with s1, s2 the first round's normalisation (1 afterwards), as the per-product kernels
-// compute them, in the same order and with the same instructions, so the results are bitwise
-// theirs. Launched as separate kernels, every product ends in a tail where the device drains
+// compute them: the same MFMA sequence per output block and the same epilogue arithmetic, so
+// the results are bitwise theirs. Launched as separate kernels, every product ends in a tail where the device drains
 // and a burst of stores that nothing overlaps, 3 x rounds times per group; here one block per
 // compute unit takes work items from a queue in dependency order and starts each as soon as
 // the matrices it reads are complete.
