@@ -35,14 +35,14 @@ def _error_flag(plan, wl):
     return int(plan.workspace[off + 512:off + 516].cpu().view(torch.int32)[0])
 
 
-def _steps(wl, fused, cfg, steps):
-    plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16", dev(),
-                    fused=fused)
-    W = [si.weight(wl, i).to(dev()) for i in range(wl.n)]
+def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16):
+    """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way)."""
+    plan = MuonPlan(wl.shapes, [dtype] * wl.n, [dtype] * wl.n, "bf16", dev(), fused=fused)
+    W = [si.weight(wl, i).to(dev(), dtype) for i in range(wl.n)]
     M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
     O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
     for t in range(steps):
-        G = [si.grad(wl, i, t).to(dev()) for i in range(wl.n)]
+        G = [si.grad(wl, i, t).to(dev(), dtype) for i in range(wl.n)]
         plan.step(W, G, M, cfg, outs=O)
         torch.cuda.synchronize()
         if fused:
@@ -71,6 +71,14 @@ def test_single_launch_768_rows_equal_per_product_launches(ns_steps):
     wl = si.custom(MID, steps=3, cfg_id=160 + ns_steps)
     cfg = make_config(ns_steps=ns_steps)
     _assert_bitwise(_steps(wl, True, cfg, 3), _steps(wl, False, cfg, 3), f"ns_steps {ns_steps}")
+
+
+def test_single_launch_fp32_parameters_and_gradients():
+    print("[fused] small set, fp32 W and G", flush=True)
+    wl = si.custom(SMALL, steps=2, cfg_id=158)
+    cfg = make_config()
+    _assert_bitwise(_steps(wl, True, cfg, 2, torch.float32),
+                    _steps(wl, False, cfg, 2, torch.float32), "fp32 W and G")
 
 
 def test_single_launch_rounds_with_a_coefficient_table():
