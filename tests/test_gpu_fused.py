@@ -151,3 +151,34 @@ def test_single_launch_failure_makes_the_step_nan(monkeypatch):
     # the next plan steps normally
     out = _steps(wl, True, cfg, 1)
     assert all(bool(torch.isfinite(x).all()) for x in out)
+
+
+def test_single_launch_long_run_bitwise():
+    """Many steps in a row (the GPT-2-124M set, 60 steps): two plans that take the single
+    launch and one with per-product launches step the same inputs; W, M and O agree bitwise
+    after every step. The single launch's items run in an order that changes from run to run,
+    so this checks that no ordering of its producers and consumers changes a result."""
+    print("[fused] gpt2_124m, 60 steps, two single-launch plans against per-product", flush=True)
+    wl = si.WORKLOADS["gpt2_124m"]
+    cfg = make_config()
+    G = [[si.grad(wl, i, t).to(dev()) for i in range(wl.n)] for t in range(2)]
+    runs = []
+    for fused in (True, True, False):
+        plan = MuonPlan(wl.shapes, [torch.bfloat16] * wl.n, [torch.bfloat16] * wl.n, "bf16",
+                        dev(), fused=fused)
+        W = [si.weight(wl, i).to(dev()) for i in range(wl.n)]
+        M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+        O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
+        runs.append((plan, W, M, O))
+    for t in range(60):
+        for plan, W, M, O in runs:
+            plan.step(W, G[t % 2], M, cfg, outs=O)
+        torch.cuda.synchronize()
+        ref = runs[2][1] + runs[2][2] + runs[2][3]
+        for k in (0, 1):
+            got = runs[k][1] + runs[k][2] + runs[k][3]
+            _assert_bitwise(got, ref, f"step {t}, single-launch plan {k}")
+    for k in (0, 1):
+        assert _error_flag(runs[k][0], wl) == 0
+    for plan, *_ in runs:
+        plan.close()
