@@ -422,6 +422,38 @@ def bench_roweq(plan, W, G, M, wl, args, ms_plain):
     return out
 
 
+def bench_per_product(wl, W, G, M, cfg, args, dev, stream):
+    """The same steps with one launch per product (the shape groups on concurrent streams),
+    the path sets take that the single launch does not: step time, and the products' nominal
+    flops over their summed kernel times from a pass with per-launch timing (where the groups
+    run one after the other)."""
+    plan = MuonPlan(wl.shapes, [w.dtype for w in W], [w.dtype for w in W], args.precision, dev,
+                    fused=False)
+    for t in range(max(args.warmup // 2, 1)):
+        plan.step(W, G[t % 2], M, cfg)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(args.steps):
+        plan.step(W, G[t % 2], M, cfg)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    plan.set_profiling(True)
+    for t in range(args.steps):
+        plan.step(W, G[t % 2], M, cfg)
+    torch.cuda.synchronize()
+    prof = plan.read_profile()
+    plan.close()
+    prod_ms = {k: prof[k][0] / args.steps for k in ("gram", "poly", "apply")}
+    total = sum(prod_ms.values())
+    peak = PEAK_BF16_TFLOPS if args.precision == "bf16" else PEAK_F32_TFLOPS
+    frac = wl.ns_flops_per_step() / (total * 1e-3) / 1e12 / peak if total > 0 else None
+    print(f"[bench] one launch per product: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    return {"ms_per_step": ms, "value": 1000.0 / ms, "products_ms_per_step": prod_ms,
+            "ns_frac_of_peak": frac}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,6 +470,8 @@ def main():
     ap.add_argument("--no-adam", action="store_true", help="skip the cautious-Adam leg")
     ap.add_argument("--no-fused", action="store_true",
                     help="one launch per product instead of all rounds in one launch")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="skip timing the other path (one launch per product) beside it")
     ap.add_argument("--no-mfma-bound", action="store_true",
                     help="skip the matrix-core issue bound of the products")
     ap.add_argument("--no-roweq", action="store_true", help="skip the row-equaliser leg")
@@ -586,6 +620,10 @@ def main():
     if not args.no_mfma_bound and args.precision == "bf16" and "kernels" in out:
         gemm_ms = sum(out["kernels"][k]["ms_per_step"] for k in NS_KINDS)
         out["mfma_bound"] = mfma_bound(wl, dev, gemm_ms, fused=not args.no_fused)
+
+    fused_used = "kernels" in out and out["kernels"].get("rounds", {}).get("launches_per_step", 0) > 0
+    if fused_used and not args.no_alt:
+        out["one_launch_per_product"] = bench_per_product(wl, W, G, M, cfg, args, dev, stream)
 
     next_rows = {}
     if not args.no_roweq:
