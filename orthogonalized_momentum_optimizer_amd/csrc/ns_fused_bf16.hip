@@ -484,6 +484,8 @@ size_t fused_sync_words(const NsGroup* groups, int n, int rounds) {
 
 hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
                              uint32_t* sync, int max_polls, hipStream_t s) {
+  // the kernel's tiles and items assume these shapes: nothing is launched otherwise
+  if (!fused_rounds_ok(groups, n, rounds) || max_polls < 0) return hipErrorInvalidValue;
   FusedLaunch F{};
   F.ng = n;
   F.rounds = rounds;
