@@ -2,7 +2,7 @@
 It computes the per-product kernels' products in their order with their instructions, so a
 step with it must give bitwise the W, momentum and O of the same step with one launch per
 product; parity with the oracle over whole trajectories is in test_gpu_trajectories.py (the
-GPT-2-124M and tall-stress sets take this launch by default). Round counts 1 and 2 check the
+GPT-2-124M set takes this launch by default). Round counts 1 and 2 check the
 ping-pong of X (the result lands in either buffer), 16 the largest the launch takes; a
 per-round coefficient table checks that each round reads its own (a, b, c)."""
 import pytest
