@@ -24,6 +24,11 @@ SMALL = [(256, 256)] * 8 + [(512, 256)] * 8 + [(256, 1024)] * 8
 # two groups of 768-row matrices (the GPT-2-124M widths at a sixth of its count): 768x768 and
 # 1536x768 (tall, runs as 768x1536)
 MID = [(768, 768)] * 8 + [(1536, 768)] * 8
+# four groups, the most the launch takes: 256x256, 256x768, 512x512 and 1024x512 (tall, runs as
+# 512x1024), with 8, 9, 16 and 11 matrices (a group whose count is not a multiple of 8 leaves
+# some XCDs one matrix fewer), interleaved in the list
+FOUR = ([(256, 256), (256, 768), (512, 512), (1024, 512)] * 8 + [(256, 768), (512, 512)]
+        + [(512, 512)] * 7 + [(1024, 512)] * 3)
 
 
 def _error_flag(plan, wl):
@@ -36,8 +41,11 @@ def _error_flag(plan, wl):
 
 
 def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16):
-    """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way)."""
+    """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way).
+    The library's launch counts confirm which path ran: the single launch once per step, or
+    no single launch and one launch per product."""
     plan = MuonPlan(wl.shapes, [dtype] * wl.n, [dtype] * wl.n, "bf16", dev(), fused=fused)
+    plan.set_profiling(True)
     W = [si.weight(wl, i).to(dev(), dtype) for i in range(wl.n)]
     M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
     O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
@@ -47,6 +55,11 @@ def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16):
         torch.cuda.synchronize()
         if fused:
             assert _error_flag(plan, wl) == 0, f"step {t}: a wait of the single launch gave up"
+    prof = plan.read_profile()
+    if fused:
+        assert prof["rounds"][1] == steps and prof["apply"][1] == 0, prof
+    else:
+        assert prof["rounds"][1] == 0 and prof["apply"][1] > 0, prof
     out = [x.clone() for x in W + M + O]
     plan.close()
     return out
@@ -71,6 +84,14 @@ def test_single_launch_768_rows_equal_per_product_launches(ns_steps):
     wl = si.custom(MID, steps=3, cfg_id=160 + ns_steps)
     cfg = make_config(ns_steps=ns_steps)
     _assert_bitwise(_steps(wl, True, cfg, 3), _steps(wl, False, cfg, 3), f"ns_steps {ns_steps}")
+
+
+@pytest.mark.parametrize("ns_steps", [2, 5])
+def test_single_launch_four_groups_equal_per_product_launches(ns_steps):
+    print(f"[fused] four groups, ns_steps={ns_steps}", flush=True)
+    wl = si.custom(FOUR, steps=2, cfg_id=180 + ns_steps)
+    cfg = make_config(ns_steps=ns_steps)
+    _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), f"ns_steps {ns_steps}")
 
 
 def test_single_launch_fp32_parameters_and_gradients():
