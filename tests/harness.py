@@ -201,12 +201,14 @@ def compare(wl, gpu, steps, precision, grads=None, report=None, oracle_kw=None):
 
 
 def run_lockstep(wl, steps, precision, watch, cfg=None, gpu_fill_others=False, oracle_kw=None,
-                 dev=None):
+                 dev=None, single_launch=None):
     """``steps`` Muon steps of the whole workload on the GPU; after each one, the oracle's
     step of every watched matrix from the oracle's own state, compared at once (nothing is
     kept but the oracle's state). Gradients of watched matrices come from the seeded CPU
     generator, once per step for both sides. Prints one line per step. Returns the worst
-    errors as ``compare`` does."""
+    errors as ``compare`` does. ``single_launch`` (True / False): after the compared steps,
+    one more step with the library's launch counts on confirms that the plan runs its
+    rounds as one persistent launch (or as one launch per product)."""
     dev = dev or torch.device("cuda", 0)
     watch = list(watch)
     kw = dict(oracle_kw or {})
@@ -235,6 +237,14 @@ def run_lockstep(wl, steps, precision, watch, cfg=None, gpu_fill_others=False, o
             es = "" if step_worst[3] is None else f" Wst {step_worst[3]:.2e}"
             print(f"[gpu] {wl.name} {precision} step {t + 1}/{steps}: O {step_worst[0]:.2e} "
                   f"W {step_worst[1]:.2e} M {step_worst[2]:.2e}{es}", flush=True)
+        if single_launch is not None:
+            plan.set_profiling(True)
+            G = [si.grad(wl, i, 0).to(dev) for i in range(wl.n)]
+            plan.step(W, G, M, cfg, outs=O)
+            torch.cuda.synchronize()
+            prof = plan.read_profile()
+            assert (prof["rounds"][1] == 1) == single_launch, prof
+            assert (prof["apply"][1] == 0) == single_launch, prof
     finally:
         plan.close()
     _summary(wl.name, precision, worst)

@@ -12,10 +12,12 @@ What is watched (matrices are independent of each other, checked bitwise elsewhe
 
 * attn_768 (1 x 768x768, 10 steps): the matrix, both precisions.
 * gpt2_124m (72 matrices, 20 steps): bf16: the first, middle and last matrix of each shape
-  (9 matrices); fp32: one matrix of each shape.
-* tall_stress (96 matrices, 20 steps): bf16: the first, middle and last of each shape, plus
-  the tall and the wide matrix whose step-0 gradient has the most row-dominated energy (one
-  row holds 57% of it in the wide one); fp32: the two outliers.
+  (9 matrices), the rounds as one persistent launch (confirmed from the library's launch
+  counts); fp32: one matrix of each shape.
+* tall_stress (96 matrices, 20 steps; one launch per product, confirmed likewise): bf16: the
+  first, middle and last of each shape, plus the tall and the wide matrix whose step-0
+  gradient has the most row-dominated energy (one row holds 57% of it in the wide one);
+  fp32: the two outliers.
 * gpt2_1p5b (288 matrices, 10 steps): bf16: all six matrices of layers 0, 24 and 47, one
   layer per test; fp32: 4 steps of one matrix of each shape in layers 0 and 47.
 """
@@ -57,7 +59,7 @@ def test_gpt2_124m_trajectory_bf16():
     wl = si.WORKLOADS["gpt2_124m"]
     watch = si.sample_indices(wl)
     _announce(f"gpt2_124m bf16, {wl.steps} steps, watch {watch}")
-    run_lockstep(wl, wl.steps, "bf16", watch)
+    run_lockstep(wl, wl.steps, "bf16", watch, single_launch=True)
 
 
 @pytest.mark.timeout(600)
@@ -73,7 +75,7 @@ def test_tall_stress_trajectory_bf16():
     wl = si.WORKLOADS["tall_stress"]
     watch = sorted(set(si.sample_indices(wl)) | set(_row_outliers(wl)))
     _announce(f"tall_stress bf16, {wl.steps} steps, watch {watch}")
-    run_lockstep(wl, wl.steps, "bf16", watch)
+    run_lockstep(wl, wl.steps, "bf16", watch, single_launch=False)
 
 
 @pytest.mark.timeout(600)
