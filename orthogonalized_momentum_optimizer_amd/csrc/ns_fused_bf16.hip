@@ -276,12 +276,14 @@ __device__ __forceinline__ void apply_tile(u32x4* smem, const ApplyWork& w, int 
 
 // ---- the queue ----
 
-__device__ __forceinline__ int local_batch(int batch, int x) {
+// The queue's arithmetic is host-callable too, so that a host program can walk every XCD's
+// queue and check the progress argument (tests/host_cpp/fused_queue_check.cpp).
+__host__ __device__ __forceinline__ int local_batch(int batch, int x) {
   return batch > x ? (batch - x + 7) / 8 : 0;
 }
 
 // Items of group g in XCD x for phase ph (Gram and polynomial: four-block items; apply: tiles).
-__device__ __forceinline__ int phase_items(const FusedGroup& G, int ph, int x) {
+__host__ __device__ __forceinline__ int phase_items(const FusedGroup& G, int ph, int x) {
   const int bx = local_batch(G.batch, x);
   if (ph == PH_APPLY) return bx * G.tiles_m * G.tiles_n;
   return quad::quad_item_count(quad::quad_items_of(bx, G.mp));
@@ -322,7 +324,8 @@ struct Item {
   int r, ph, g, i;  // round, phase, group, item of the group's XCD share in that phase
 };
 
-__device__ __forceinline__ Item decode(const FusedLaunch& F, int idx, int per_round, int x) {
+__host__ __device__ __forceinline__ Item decode(const FusedLaunch& F, int idx, int per_round,
+                                                int x) {
   Item it;
   it.r = idx / per_round;
   int rem = idx - it.r * per_round;
@@ -342,6 +345,44 @@ __device__ __forceinline__ Item decode(const FusedLaunch& F, int idx, int per_ro
       rem -= n;
     }
   return it;  // not reached: idx < rounds * per_round
+}
+
+// The completion counters an item reads before it starts and the count each must reach:
+// apply tiles the polynomial's counter of their matrix (every upper block stored), the
+// polynomial's items the Gram counters of the two matrices their waves load (m0, m2; the
+// same counter twice when they are one matrix), a later round's Gram items the previous
+// round's apply counters (4 per tile: each wave of a tile adds 1). The first round's Gram
+// items read X_0, complete before the launch (n = 0).
+struct Deps {
+  uint32_t* c[2];
+  uint32_t target;
+  int n;
+};
+
+__host__ __device__ __forceinline__ Deps item_deps(const FusedLaunch& F, const Item& it, int x) {
+  const FusedGroup& G = F.g[it.g];
+  const size_t row = (size_t)G.batch;
+  Deps d;
+  d.n = 0;
+  d.target = 0;
+  d.c[0] = d.c[1] = nullptr;
+  if (it.ph == PH_APPLY) {
+    const int j = it.i / (G.tiles_m * G.tiles_n);
+    d.c[0] = G.cnt + ((size_t)PH_POLY * F.rounds + it.r) * row + (x + 8 * j);
+    d.target = G.nblk;
+    d.n = 1;
+  } else if (it.ph == PH_POLY || it.r > 0) {
+    const quad::QuadItems qi = quad::quad_items_of(local_batch(G.batch, x), G.mp);
+    const int m0 = x + 8 * quad::quad_wave(qi, it.i, 0).lmat;
+    const int m2 = x + 8 * quad::quad_wave(qi, it.i, 3).lmat;
+    uint32_t* c = it.ph == PH_POLY ? G.cnt + ((size_t)PH_GRAM * F.rounds + it.r) * row
+                                   : G.cnt + ((size_t)PH_APPLY * F.rounds + it.r - 1) * row;
+    d.c[0] = c + m0;
+    d.c[1] = c + m2;
+    d.target = it.ph == PH_POLY ? (uint32_t)G.nblk : 4u * G.tiles_m * G.tiles_n;
+    d.n = 2;
+  }
+  return d;
 }
 
 __global__ __launch_bounds__(256) void ns_fused_bf16(FusedLaunch) {
@@ -376,28 +417,8 @@ __global__ __launch_bounds__(256) void ns_fused_bf16(FusedLaunch) {
       if (idx < total) {
         // wait for what the item reads (its loads then bypass the L1: kCoherent); the L1
         // invalidation is kept for any other read of the launch's own data
-        const Item it = decode(F, idx, per_round, x);
-        const FusedGroup& G = F.g[it.g];
-        const size_t row = (size_t)G.batch;
-        if (it.ph == PH_APPLY) {
-          const int j = it.i / (G.tiles_m * G.tiles_n);
-          wait_count(G.cnt + ((size_t)PH_POLY * F.rounds + it.r) * row + (x + 8 * j), G.nblk,
-                     F.err, F.max_polls);
-        } else {
-          const quad::QuadItems qi = quad::quad_items_of(local_batch(G.batch, x), G.mp);
-          const int m0 = x + 8 * quad::quad_wave(qi, it.i, 0).lmat;
-          const int m2 = x + 8 * quad::quad_wave(qi, it.i, 3).lmat;
-          if (it.ph == PH_POLY) {
-            uint32_t* c = G.cnt + ((size_t)PH_GRAM * F.rounds + it.r) * row;
-            wait_count(c + m0, G.nblk, F.err, F.max_polls);
-            wait_count(c + m2, G.nblk, F.err, F.max_polls);
-          } else if (it.r > 0) {
-            uint32_t* c = G.cnt + ((size_t)PH_APPLY * F.rounds + it.r - 1) * row;
-            const uint32_t tiles4 = 4u * G.tiles_m * G.tiles_n;
-            wait_count(c + m0, tiles4, F.err, F.max_polls);
-            wait_count(c + m2, tiles4, F.err, F.max_polls);
-          }
-        }
+        const Deps d = item_deps(F, decode(F, idx, per_round, x), x);
+        for (int k = 0; k < d.n; ++k) wait_count(d.c[k], d.target, F.err, F.max_polls);
         asm volatile("buffer_inv sc0" ::: "memory");
         vm_wait<0>();
       }
@@ -482,10 +503,13 @@ size_t fused_sync_words(const NsGroup* groups, int n, int rounds) {
   return w;
 }
 
-hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
-                             uint32_t* sync, int max_polls, hipStream_t s) {
-  // the kernel's tiles and items assume these shapes: nothing is launched otherwise
-  if (!fused_rounds_ok(groups, n, rounds) || max_polls < 0) return hipErrorInvalidValue;
+namespace {
+
+// The launch's arguments for groups that fused_rounds_ok accepts: per-group buffers and item
+// counts, the completion counters laid out after the queues and the error flag in `sync`,
+// and each phase's group order.
+FusedLaunch make_fused_launch(const NsGroup* groups, int n, int rounds, const float* abc,
+                              uint32_t* sync, int max_polls) {
   FusedLaunch F{};
   F.ng = n;
   F.rounds = rounds;
@@ -523,6 +547,16 @@ hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const flo
     F.ord[PH_POLY][k] = o[n - 1 - k];
     F.ord[PH_APPLY][k] = o[n - 1 - k];
   }
+  return F;
+}
+
+}  // namespace
+
+hipError_t launch_fused_bf16(const NsGroup* groups, int n, int rounds, const float* abc,
+                             uint32_t* sync, int max_polls, hipStream_t s) {
+  // the kernel's tiles and items assume these shapes: nothing is launched otherwise
+  if (!fused_rounds_ok(groups, n, rounds) || max_polls < 0) return hipErrorInvalidValue;
+  const FusedLaunch F = make_fused_launch(groups, n, rounds, abc, sync, max_polls);
   const int words = (int)fused_sync_words(groups, n, rounds);
   launch_k(fused_clear, dim3((words + 255) / 256), dim3(256), 0, s, sync, words);
   if (hipError_t e = hipGetLastError()) return e;
