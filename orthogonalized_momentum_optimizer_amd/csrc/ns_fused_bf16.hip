@@ -349,10 +349,10 @@ __host__ __device__ __forceinline__ Item decode(const FusedLaunch& F, int idx, i
 
 // The completion counters an item reads before it starts and the count each must reach:
 // apply tiles the polynomial's counter of their matrix (every upper block stored), the
-// polynomial's items the Gram counters of the two matrices their waves load (m0, m2; the
-// same counter twice when they are one matrix), a later round's Gram items the previous
-// round's apply counters (4 per tile: each wave of a tile adds 1). The first round's Gram
-// items read X_0, complete before the launch (n = 0).
+// polynomial's items the Gram counters of the matrices their waves load (m0 for waves 0-1,
+// m2 for waves 2-3; one counter when they are one matrix), a later round's Gram items the
+// previous round's apply counters of those matrices (4 per tile: each wave of a tile adds
+// 1). The first round's Gram items read X_0, complete before the launch (n = 0).
 struct Deps {
   uint32_t* c[2];
   uint32_t target;
@@ -380,7 +380,7 @@ __host__ __device__ __forceinline__ Deps item_deps(const FusedLaunch& F, const I
     d.c[0] = c + m0;
     d.c[1] = c + m2;
     d.target = it.ph == PH_POLY ? (uint32_t)G.nblk : 4u * G.tiles_m * G.tiles_n;
-    d.n = 2;
+    d.n = m0 == m2 ? 1 : 2;
   }
   return d;
 }

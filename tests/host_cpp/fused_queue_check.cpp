@@ -109,7 +109,8 @@ static long long check_set(const std::vector<NsGroup>& groups, int rounds) {
           if (it.ph == PH_POLY) reads.push_back(x + 8 * qw.omat);  // its b A term
         }
         const bool first_gram = it.ph == PH_GRAM && it.r == 0;
-        CHECK(d.n == (first_gram ? 0 : 2), "xcd %d item %d: %d counters\n", x, idx, d.n);
+        CHECK(first_gram ? d.n == 0 : (d.n == 1 || d.n == 2), "xcd %d item %d: %d counters\n",
+              x, idx, d.n);
       }
       if (d.n == 0) continue;
       // the phase and round whose outputs the item reads
