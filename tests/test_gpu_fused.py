@@ -40,17 +40,17 @@ def _error_flag(plan, wl):
     return int(plan.workspace[off + 512:off + 516].cpu().view(torch.int32)[0])
 
 
-def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16):
-    """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way).
-    The library's launch counts confirm which path ran: the single launch once per step, or
-    no single launch and one launch per product."""
+def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16, scale=1.0):
+    """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way),
+    the seeded gradients multiplied by `scale`. The library's launch counts confirm which path
+    ran: the single launch once per step, or no single launch and one launch per product."""
     plan = MuonPlan(wl.shapes, [dtype] * wl.n, [dtype] * wl.n, "bf16", dev(), fused=fused)
     plan.set_profiling(True)
     W = [si.weight(wl, i).to(dev(), dtype) for i in range(wl.n)]
     M = [torch.zeros(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
     O = [torch.empty(s, dtype=torch.float32, device=dev()) for s in wl.shapes]
     for t in range(steps):
-        G = [si.grad(wl, i, t).to(dev(), dtype) for i in range(wl.n)]
+        G = [(si.grad(wl, i, t).float() * scale).to(dev(), dtype) for i in range(wl.n)]
         plan.step(W, G, M, cfg, outs=O)
         torch.cuda.synchronize()
         if fused:
@@ -92,6 +92,22 @@ def test_single_launch_four_groups_equal_per_product_launches(ns_steps):
     wl = si.custom(FOUR, steps=2, cfg_id=180 + ns_steps)
     cfg = make_config(ns_steps=ns_steps)
     _assert_bitwise(_steps(wl, True, cfg, 2), _steps(wl, False, cfg, 2), f"ns_steps {ns_steps}")
+
+
+@pytest.mark.parametrize("scale,eps", [(1e-22, 0.0), (1e-22, 1e-7), (1e22, 1e-7)])
+def test_single_launch_extreme_gradient_scales(scale, eps):
+    """Gradient entries near 1e-25 and 1e19: the norm kernel rescales X_0 by a power of two
+    before the rounds (its fp32 Gram accumulation would underflow or overflow otherwise), and
+    the single launch then runs on the rescaled X_0 with the adjusted s1. Bitwise the per-
+    product launches' result, and O finite (with eps = 1e-7 the small gradients' O is the
+    rounds applied to U / eps, small but not zero)."""
+    print(f"[fused] small set, gradient scale {scale:g}, eps {eps:g}", flush=True)
+    wl = si.custom(SMALL, steps=2, cfg_id=190)
+    cfg = make_config(eps=eps)
+    fused = _steps(wl, True, cfg, 2, scale=scale)
+    _assert_bitwise(fused, _steps(wl, False, cfg, 2, scale=scale), f"scale {scale:g}")
+    O = fused[2 * wl.n:]
+    assert all(bool(torch.isfinite(o).all()) and bool(o.abs().max() > 0) for o in O)
 
 
 def test_single_launch_fp32_parameters_and_gradients():
