@@ -40,10 +40,12 @@ def _error_flag(plan, wl):
     return int(plan.workspace[off + 512:off + 516].cpu().view(torch.int32)[0])
 
 
-def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16, scale=1.0):
+def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16, scale=1.0, single=None):
     """W, M and O after `steps` steps; W and G in `dtype` (the rounds are bf16 either way),
     the seeded gradients multiplied by `scale`. The library's launch counts confirm which path
-    ran: the single launch once per step, or no single launch and one launch per product."""
+    ran (`single`, by default `fused`): the single launch once per step, or no single launch
+    and one launch per product."""
+    single = fused if single is None else single
     plan = MuonPlan(wl.shapes, [dtype] * wl.n, [dtype] * wl.n, "bf16", dev(), fused=fused)
     plan.set_profiling(True)
     W = [si.weight(wl, i).to(dev(), dtype) for i in range(wl.n)]
@@ -53,10 +55,10 @@ def _steps(wl, fused, cfg, steps, dtype=torch.bfloat16, scale=1.0):
         G = [(si.grad(wl, i, t).float() * scale).to(dev(), dtype) for i in range(wl.n)]
         plan.step(W, G, M, cfg, outs=O)
         torch.cuda.synchronize()
-        if fused:
+        if single:
             assert _error_flag(plan, wl) == 0, f"step {t}: a wait of the single launch gave up"
     prof = plan.read_profile()
-    if fused:
+    if single:
         assert prof["rounds"][1] == steps and prof["apply"][1] == 0, prof
     else:
         assert prof["rounds"][1] == 0 and prof["apply"][1] > 0, prof
@@ -108,6 +110,16 @@ def test_single_launch_extreme_gradient_scales(scale, eps):
     _assert_bitwise(fused, _steps(wl, False, cfg, 2, scale=scale), f"scale {scale:g}")
     O = fused[2 * wl.n:]
     assert all(bool(torch.isfinite(o).all()) and bool(o.abs().max() > 0) for o in O)
+
+
+def test_more_rounds_than_the_single_launch_takes():
+    """17 rounds, one more than the launch's round table holds: a plan with the single launch
+    enabled runs one launch per product instead, with the same results."""
+    print("[fused] small set, ns_steps=17: one launch per product", flush=True)
+    wl = si.custom(SMALL, steps=1, cfg_id=195)
+    cfg = make_config(ns_steps=17)
+    _assert_bitwise(_steps(wl, True, cfg, 1, single=False), _steps(wl, False, cfg, 1),
+                    "ns_steps 17")
 
 
 def test_single_launch_fp32_parameters_and_gradients():
